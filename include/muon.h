@@ -1,0 +1,190 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon-style optimizer step.
+ *
+ * The method (page "きみはNanoGPT speedrunを知っているか？", prednext.com,
+ * section "Muonとは"; the neo-ai.one article on the Muon author, section
+ * "Muonが登場"): keep a moving average (momentum) of each 2-D weight matrix's
+ * gradient, approximately orthogonalise that momentum with Newton-Schulz
+ * iteration so that its singular values move towards one, and update the
+ * weights with the result.  The iteration implemented is the odd polynomial
+ *     X <- a_j X + (b_j A + c_j A^2) X,   A = X X^T,   j = 0 .. steps-1,
+ * run on the wide orientation of each matrix (tall matrices are transposed so
+ * that A is the smaller Gram matrix) after dividing by (||X||_F + eps).
+ * Options cover the variant of page "Training NanoGPT in 39.9 Seconds"
+ * (seosoyoung.eiaserinnys.me digest), section "ANVIL II와 가중치 평균": a fast
+ * and a slow momentum, a fixed number of polynomial-map steps, weight decay
+ * applied only where the weight agrees in sign with the slow momentum, and an
+ * exponential moving average of the weights (the section's displayed
+ * equation) with a final readout blend of final weights and average.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major device buffers: element (i, j) of a muon_mat lives
+ *     at ptr[i*ld + j].  ld >= cols.  Pointers must be 16-byte aligned.
+ *   - The caller owns all device memory (parameters, gradients, optimizer
+ *     state, workspace).  Host arrays passed in are read during the call only.
+ *     The library allocates no device memory; it keeps a host-side plan cache.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream)
+ *     and the call returns without synchronising.
+ *   - Every argument is validated before the first launch.  On any error the
+ *     function returns a nonzero MUON_E_* code, enqueues nothing and leaves
+ *     the state and its counters unchanged.  MUON_E_HIP means a HIP call
+ *     failed after validation; device buffers are then undefined and the
+ *     counters are not advanced.
+ *   - A state must not be used from two host threads at once.  Calls on one
+ *     workspace must be ordered on one stream.
+ *   - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { MUON_BF16 = 0, MUON_F32 = 1 };
+
+/* status codes */
+enum {
+  MUON_OK = 0,
+  MUON_E_NULL = 1,       /* a required pointer is NULL                          */
+  MUON_E_SHAPE = 2,      /* n < 0, rows/cols < 1, ld < cols, shapes differ      */
+  MUON_E_DTYPE = 3,      /* unknown element type                                */
+  MUON_E_COEFFS = 4,     /* steps outside [0, MUON_MAX_STEPS] or non-finite a,b,c */
+  MUON_E_HPARAM = 5,     /* non-finite lr/wd/eps, beta outside [0,1), bad option */
+  MUON_E_WORKSPACE = 6,  /* workspace NULL or smaller than muon_workspace_bytes  */
+  MUON_E_ALIAS = 7,      /* two buffers that must be distinct overlap          */
+  MUON_E_ALIGN = 8,      /* a pointer or row pitch breaks 16-byte alignment    */
+  MUON_E_HIP = 9,        /* a HIP runtime call failed                           */
+  MUON_E_STATE = 10      /* state inconsistent with the call (n, buffers)       */
+};
+
+#define MUON_MAX_STEPS 16
+
+/* One 2-D matrix on the device. */
+typedef struct {
+  void*   ptr;     /* device pointer, row-major                                */
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;      /* row pitch in elements; ld*element_size % 16 == 0        */
+  int32_t dtype;   /* MUON_BF16 or MUON_F32                                    */
+  int32_t _pad;
+} muon_mat;
+
+/* Options of the step; muon_default_options() fills the plain-Muon defaults. */
+typedef struct {
+  float   beta_slow;  /* slow momentum coefficient in [0,1); < 0 disables it   */
+  float   beta_ema;   /* weight-average coefficient in [0,1); < 0 disables it  */
+  float   eps;        /* added to the Frobenius norm (default 1e-7)            */
+  int32_t nesterov;   /* 1: orthogonalise beta*M_t + (1-beta)*G instead of M_t */
+  int64_t ema_start;  /* first step (1-based, after increment) that is averaged */
+  int32_t cautious;   /* 1: decay only where W_{t-1} and S_t share a strict sign
+                         (needs beta_slow >= 0)                                */
+  int32_t ns_dtype;   /* MUON_BF16: bf16 MFMA operands with fp32 accumulation;
+                         MUON_F32: fp32 operands and accumulation              */
+} muon_options;
+
+/* Optimizer state.  The buffer arrays are HOST arrays of n DEVICE pointers;
+ * every buffer is fp32, dense row-major rows x cols of the matching param. */
+typedef struct {
+  int32_t   n;            /* number of matrices                                */
+  int32_t   _pad;
+  float**   mom;          /* momentum (required)                               */
+  float**   mom_slow;     /* slow momentum; required iff opt.beta_slow >= 0    */
+  float**   ema;          /* weight average; required iff opt.beta_ema >= 0    */
+  uint8_t** mask_out;     /* optional diagnostic (NULL = off): per matrix, a
+                             dense rows x cols byte array receiving the decay
+                             mask actually applied (1 = decayed)               */
+  float**   update_out;   /* optional diagnostic (NULL = off): per matrix, a
+                             dense rows x cols fp32 array receiving the
+                             orthogonalised update O actually applied          */
+  void*     workspace;    /* device scratch of >= muon_workspace_bytes bytes   */
+  size_t    workspace_bytes;
+  int64_t   step;         /* number of completed steps (incremented per call)  */
+  int64_t   ema_count;    /* number of steps folded into the weight average    */
+  muon_options opt;
+} muon_state;
+
+/* Plain-Muon defaults: no slow momentum, no EMA, eps 1e-7, ema_start 1,
+ * no Nesterov, no cautious decay, bf16 MFMA Newton-Schulz. */
+void muon_default_options(muon_options* opt);
+
+/* Workspace bytes needed by muon_step / muon_orthogonalize for this list of
+ * matrix shapes (only rows and cols of params[] are read) and options.
+ * `steps` is accepted for symmetry; the size does not depend on it.
+ * Returns 0 if the arguments are invalid. */
+size_t muon_workspace_bytes(const muon_mat* params, int32_t n,
+                            const muon_options* opt, int32_t steps);
+
+/* One optimizer step over n matrices (the whole hot path):
+ *   M <- beta*M + (1-beta)*G                       (fp32, no fused ops)
+ *   S <- beta_slow*S + (1-beta_slow)*G             (if enabled)
+ *   U  = M, or beta*M + (1-beta)*G with Nesterov
+ *   O  = orthogonalise(U) with `steps` rows of coeffs (a_j, b_j, c_j)
+ *   W <- W - lr*wd*mask*W - lr*O   (mask = 1, or [W*S > 0] when cautious)
+ *   step += 1;  if EMA enabled and step >= ema_start:
+ *       E <- W (first averaged step) or beta_ema*E + (1-beta_ema)*W;
+ *       ema_count += 1
+ * params: n matrices, updated in place (bf16 is rounded to nearest even).
+ * grads:  n matrices with the same shapes (any element type).
+ * coeffs: HOST array of steps*3 floats.  steps in [0, MUON_MAX_STEPS].
+ * lr, wd finite; beta in [0,1).  n == 0 only advances the counters. */
+int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
+              const float* coeffs, int32_t steps, float lr, float wd,
+              float beta, void* stream);
+
+/* Newton-Schulz part alone: out[i] = orthogonalise(in[i]) for n matrices
+ * (same shapes; out may be any element type; in and out must not overlap).
+ * Uses opt->eps and opt->ns_dtype; the other options are ignored. */
+int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n,
+                       const float* coeffs, int32_t steps,
+                       const muon_options* opt, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Readout blend out[i] = w_final*W[i] + (1-w_final)*E[i] (fp32 operation
+ * order, rounded to out's element type), with E the state's weight average
+ * (page "Training NanoGPT in 39.9 Seconds", section "ANVIL II와 가중치 평균":
+ * 35 % final weights and 65 % average, i.e. w_final = 0.35).
+ * Requires st->ema; w_final in [0,1]. */
+int muon_ema_blend(const muon_mat* out, const muon_mat* params,
+                   const muon_state* st, float w_final, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* muon_status_str(int status);
+
+/* ---------------------------------------------------------------------------
+ * Measurement hooks.  A phase's kernel launches can be bracketed with HIP
+ * events recorded on the launch stream; used to time one kernel inside a
+ * running step.  Not needed for normal use. */
+enum {
+  MUON_PHASE_PREPARE = 0,  /* momentum, cast/transpose, norm partials */
+  MUON_PHASE_GRAM = 1,     /* A = X X^T                               */
+  MUON_PHASE_POLY = 2,     /* B = b A + c A^2                         */
+  MUON_PHASE_APPLY = 3,    /* X <- a X + B X                          */
+  MUON_PHASE_FINISH = 4    /* update, mask, EMA (or write O)          */
+};
+
+/* Record events around each of the next `capacity` launches of `phase`
+ * (capacity in [1, 65536]).  Re-arming discards earlier records. */
+int muon_probe_arm(int32_t phase, int32_t capacity);
+/* Wait for the recorded events and write up to `capacity` per-launch
+ * durations in milliseconds to ms[]; *count receives the number recorded. */
+int muon_probe_read(float* ms, int32_t capacity, int32_t* count);
+/* Stop recording and release the events. */
+int muon_probe_disarm(void);
+
+/* Kernel configuration chosen for a shape list: number of effective-shape
+ * groups, Newton-Schulz tile size per group (in `tiles`, up to `cap`
+ * entries), and launches per step for `steps` iterations with coefficient
+ * table `coeffs` (host, may be NULL for quintic). Returns a status. */
+int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt,
+                   int32_t steps, const float* coeffs, int32_t* n_groups,
+                   int32_t* tiles, int32_t cap, int32_t* launches_per_step);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,724 @@
+// C ABI of the Muon step library: validation, planning, launch sequencing.
+//
+// The method and its options are stated in include/muon.h.  This file holds
+// no arithmetic of the step; it checks arguments, groups the matrices by
+// effective shape (m, n) = (min(rows, cols), max(rows, cols)), lays out the
+// caller's workspace, keeps the device descriptor table current and enqueues
+// the kernels on the caller's stream:
+//   prepare -> [GRAM -> (POLY) -> APPLY] x steps -> finish.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_common.h"
+
+using namespace muon;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kCUs = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+int esize(int dt) { return dt == MUON_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- planning
+struct GroupPlan {
+  int m = 0, n = 0, mp = 0, np = 0;
+  std::vector<int> mats;
+  size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0, off_part = 0;
+  int64_t x_elems = 0, a_elems = 0;
+  int npart = 0;
+};
+
+struct Plan {
+  int xdt = MUON_BF16;
+  int ts = 256;
+  std::vector<GroupPlan> groups;
+  std::vector<int> mat_group, mat_slot;
+  size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
+  std::vector<int64_t> pprefix, fprefix;
+};
+
+// Relative throughput of a tile edge (larger tiles reuse operands more).
+double tile_eff(int ts) { return ts == 256 ? 1.0 : ts == 128 ? 0.75 : 0.45; }
+
+// Estimated time units of one step's products for tile edge ts: each phase
+// runs in ceil(tiles / CUs) waves of its largest tile.
+double plan_cost(const std::vector<std::pair<std::pair<int, int>, int>>& shapes, int ts) {
+  double gram = 0, poly = 0, apply = 0, gmax = 0, pmax = 0, amax = 0;
+  int64_t gt = 0, pt = 0, at = 0;
+  for (auto& s : shapes) {
+    const int64_t mp = round_up(s.first.first, ts), np = round_up(s.first.second, ts);
+    const int64_t cnt = s.second, tm = mp / ts, tn = np / ts;
+    const double tile_g = double(ts) * ts * np, tile_p = double(ts) * ts * mp;
+    gt += cnt * tm * (tm + 1) / 2; pt += cnt * tm * (tm + 1) / 2; at += cnt * tm * tn;
+    gram += cnt * tm * (tm + 1) / 2 * tile_g;
+    poly += cnt * tm * (tm + 1) / 2 * tile_p;
+    apply += cnt * tm * tn * tile_p;
+    gmax = std::max(gmax, tile_g); pmax = std::max(pmax, tile_p); amax = std::max(amax, tile_p);
+  }
+  auto phase = [](double work, double tmax, int64_t tiles) {
+    const double waves = std::ceil(double(tiles) / kCUs);
+    return std::max(work / kCUs, waves * tmax);
+  };
+  return (phase(gram, gmax, gt) + phase(poly, pmax, pt) + phase(apply, amax, at)) / tile_eff(ts);
+}
+
+int choose_ts(const std::vector<std::pair<std::pair<int, int>, int>>& shapes) {
+  if (const char* e = std::getenv("MUON_TILE")) {
+    const int v = std::atoi(e);
+    if (v == 64 || v == 128 || v == 256) return v;
+  }
+  int best = 256;
+  double bc = plan_cost(shapes, 256);
+  for (int ts : {128, 64}) {
+    const double c = plan_cost(shapes, ts);
+    if (c < bc * 0.999) { bc = c; best = ts; }
+  }
+  return best;
+}
+
+void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& p) {
+  p = Plan();
+  p.xdt = xdt;
+  std::map<std::pair<int, int>, int> gidx;
+  p.mat_group.resize(n);
+  p.mat_slot.resize(n);
+  for (int i = 0; i < n; ++i) {
+    const int m = int(std::min(rows[i], cols[i])), nn = int(std::max(rows[i], cols[i]));
+    auto key = std::make_pair(m, nn);
+    auto it = gidx.find(key);
+    int g;
+    if (it == gidx.end()) {
+      g = int(p.groups.size());
+      gidx[key] = g;
+      p.groups.emplace_back();
+      p.groups.back().m = m;
+      p.groups.back().n = nn;
+    } else {
+      g = it->second;
+    }
+    p.mat_group[i] = g;
+    p.mat_slot[i] = int(p.groups[g].mats.size());
+    p.groups[g].mats.push_back(i);
+  }
+  std::vector<std::pair<std::pair<int, int>, int>> shapes;
+  for (auto& g : p.groups) shapes.push_back({{g.m, g.n}, int(g.mats.size())});
+  p.ts = choose_ts(shapes);
+
+  const int es = esize(xdt);
+  size_t off = 0;
+  p.off_desc = off;
+  off = align_up(off + sizeof(MatDesc) * size_t(n), kAlign);
+  p.off_pprefix = off;
+  off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
+  p.off_fprefix = off;
+  off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
+  for (auto& g : p.groups) {
+    g.mp = int(round_up(g.m, p.ts));
+    g.np = int(round_up(g.n, p.ts));
+    g.x_elems = int64_t(g.mp) * g.np;
+    g.a_elems = int64_t(g.mp) * g.mp;
+    g.npart = (g.mp / kEw) * (g.np / kEw);
+    const size_t cnt = g.mats.size();
+    g.off_x0 = off; off = align_up(off + cnt * g.x_elems * es, kAlign);
+    g.off_x1 = off; off = align_up(off + cnt * g.x_elems * es, kAlign);
+    g.off_a = off;  off = align_up(off + cnt * g.a_elems * es, kAlign);
+    g.off_b = off;  off = align_up(off + cnt * g.a_elems * es, kAlign);
+    g.off_part = off; off = align_up(off + cnt * size_t(g.npart) * 4, kAlign);
+  }
+  p.total = off;
+  p.pprefix.assign(n + 1, 0);
+  p.fprefix.assign(n + 1, 0);
+  for (int i = 0; i < n; ++i) {
+    const GroupPlan& g = p.groups[p.mat_group[i]];
+    p.pprefix[i + 1] = p.pprefix[i] + g.npart;
+    p.fprefix[i + 1] = p.fprefix[i] + ((rows[i] + kEw - 1) / kEw) * ((cols[i] + kEw - 1) / kEw);
+  }
+}
+
+// Plans cached by (shape list, iterate type, tile override).
+std::mutex g_mu;
+std::map<std::tuple<std::vector<int64_t>, int, int>, Plan> g_plans;
+
+const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
+  std::vector<int64_t> key(2 * size_t(n));
+  for (int i = 0; i < n; ++i) { key[2 * i] = rows[i]; key[2 * i + 1] = cols[i]; }
+  const char* e = std::getenv("MUON_TILE");
+  const int tile_env = e ? std::atoi(e) : 0;
+  auto k = std::make_tuple(std::move(key), xdt, tile_env);
+  auto it = g_plans.find(k);
+  if (it != g_plans.end()) return it->second;
+  Plan p;
+  build_plan(rows, cols, n, xdt, p);
+  if (g_plans.size() > 64) g_plans.clear();
+  return g_plans.emplace(std::move(k), std::move(p)).first->second;
+}
+
+// Device table uploads, cached per workspace so unchanged tables are not re-sent.
+struct Upload {
+  std::vector<uint8_t> bytes;
+  void* pinned = nullptr;
+  size_t cap = 0;
+};
+std::map<void*, Upload> g_uploads;
+
+hipError_t upload_table(void* ws, const std::vector<uint8_t>& bytes, hipStream_t s) {
+  Upload& u = g_uploads[ws];
+  if (u.bytes == bytes) return hipSuccess;
+  hipError_t err;
+  if (u.pinned) {
+    // the previous copy from this buffer may still be queued
+    if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;
+  }
+  if (u.cap < bytes.size()) {
+    if (u.pinned) (void)hipHostFree(u.pinned);
+    u.pinned = nullptr;
+    u.cap = 0;
+    if ((err = hipHostMalloc(&u.pinned, bytes.size(), hipHostMallocDefault)) != hipSuccess)
+      return err;
+    u.cap = bytes.size();
+  }
+  std::memcpy(u.pinned, bytes.data(), bytes.size());
+  err = hipMemcpyAsync(ws, u.pinned, bytes.size(), hipMemcpyHostToDevice, s);
+  if (err != hipSuccess) { u.bytes.clear(); return err; }
+  u.bytes = bytes;
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- probes
+struct Probe {
+  int phase = -1;
+  int cap = 0, used = 0;
+  std::vector<hipEvent_t> ev0, ev1;
+} g_probe;
+
+void probe_begin(int phase, hipStream_t s) {
+  if (g_probe.phase == phase && g_probe.used < g_probe.cap)
+    (void)hipEventRecord(g_probe.ev0[g_probe.used], s);
+}
+void probe_end(int phase, hipStream_t s) {
+  if (g_probe.phase == phase && g_probe.used < g_probe.cap)
+    (void)hipEventRecord(g_probe.ev1[g_probe.used++], s);
+}
+
+// ---------------------------------------------------------------- validation
+bool finite(float v) { return std::isfinite(v); }
+
+int check_mat(const muon_mat& m) {
+  if (!m.ptr) return MUON_E_NULL;
+  if (m.dtype != MUON_BF16 && m.dtype != MUON_F32) return MUON_E_DTYPE;
+  if (m.rows < 1 || m.cols < 1 || m.ld < m.cols) return MUON_E_SHAPE;
+  if (m.rows > (int64_t(1) << 30) || m.cols > (int64_t(1) << 30)) return MUON_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(m.ptr) % esize(m.dtype)) return MUON_E_ALIGN;
+  return MUON_OK;
+}
+
+size_t mat_bytes(const muon_mat& m) {
+  return size_t((m.rows - 1) * m.ld + m.cols) * esize(m.dtype);
+}
+
+bool vec_ok(const void* p, int64_t ld, int es) {
+  return reinterpret_cast<uintptr_t>(p) % 16 == 0 && (ld * es) % 16 == 0;
+}
+
+struct Range { uintptr_t lo, hi; };
+
+bool overlaps(std::vector<Range>& r) {
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i)
+    if (r[i].lo < r[i - 1].hi) return true;
+  return false;
+}
+
+void add_range(std::vector<Range>& r, const void* p, size_t bytes) {
+  if (p && bytes) r.push_back({reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + bytes});
+}
+
+int check_opt(const muon_options& o) {
+  if (!finite(o.eps) || o.eps < 0.f) return MUON_E_HPARAM;
+  if (o.beta_slow >= 0.f && !(o.beta_slow < 1.f)) return MUON_E_HPARAM;
+  if (o.beta_ema >= 0.f && !(o.beta_ema < 1.f)) return MUON_E_HPARAM;
+  if (!finite(o.beta_slow) || !finite(o.beta_ema)) return MUON_E_HPARAM;
+  if (o.ns_dtype != MUON_BF16 && o.ns_dtype != MUON_F32) return MUON_E_DTYPE;
+  if (o.cautious && o.beta_slow < 0.f) return MUON_E_HPARAM;
+  if (o.nesterov != 0 && o.nesterov != 1) return MUON_E_HPARAM;
+  if (o.cautious != 0 && o.cautious != 1) return MUON_E_HPARAM;
+  return MUON_OK;
+}
+
+int check_coeffs(const float* c, int steps) {
+  if (steps < 0 || steps > MUON_MAX_STEPS) return MUON_E_COEFFS;
+  if (steps > 0 && !c) return MUON_E_NULL;
+  for (int i = 0; i < 3 * steps; ++i)
+    if (!finite(c[i])) return MUON_E_COEFFS;
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------- launches
+void fill_desc(MatDesc& d, const Plan& p, int i, const muon_mat& src_shape, char* ws) {
+  const GroupPlan& g = p.groups[p.mat_group[i]];
+  const int slot = p.mat_slot[i];
+  const int es = esize(p.xdt);
+  d.rows = int(src_shape.rows);
+  d.cols = int(src_shape.cols);
+  d.mp = g.mp;
+  d.np = g.np;
+  d.tall = src_shape.rows > src_shape.cols;
+  d.x0 = ws + g.off_x0 + size_t(slot) * g.x_elems * es;
+  d.x1 = ws + g.off_x1 + size_t(slot) * g.x_elems * es;
+  d.partials = reinterpret_cast<float*>(ws + g.off_part) + size_t(slot) * g.npart;
+  d.npartials = g.npart;
+  d.dvec = (src_shape.cols % 4) == 0;
+}
+
+void table_bytes(const Plan& p, const std::vector<MatDesc>& desc, std::vector<uint8_t>& out) {
+  const int n = int(desc.size());
+  out.assign(p.off_fprefix + sizeof(int64_t) * size_t(n + 1), 0);
+  std::memcpy(out.data() + p.off_desc, desc.data(), sizeof(MatDesc) * size_t(n));
+  std::memcpy(out.data() + p.off_pprefix, p.pprefix.data(), sizeof(int64_t) * size_t(n + 1));
+  std::memcpy(out.data() + p.off_fprefix, p.fprefix.data(), sizeof(int64_t) * size_t(n + 1));
+}
+
+// Newton-Schulz iterations; returns the buffer index holding the result.
+hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float eps,
+                  hipStream_t s, int* final_buf) {
+  int cur = 0;
+  for (int j = 0; j < steps; ++j) {
+    const float a = coeffs[3 * j], b = coeffs[3 * j + 1], c = coeffs[3 * j + 2];
+    const bool poly = c != 0.f;
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.first = j == 0;
+    ga.ca = a; ga.cb = b; ga.cc = c;
+    ga.cbb = poly ? 1.f : b;
+    ga.eps = eps;
+    const int es = esize(p.xdt);
+    // groups are processed in launch sets of at most kMaxGroups
+    for (size_t g0 = 0; g0 < p.groups.size(); g0 += kMaxGroups) {
+      const size_t g1 = std::min(p.groups.size(), g0 + kMaxGroups);
+      for (int phase = 0; phase < 3; ++phase) {
+        if (phase == 1 && !poly) continue;
+        int64_t blocks = 0;
+        ga.ngroups = int(g1 - g0);
+        for (size_t gi = g0; gi < g1; ++gi) {
+          const GroupPlan& g = p.groups[gi];
+          GemmGroup& d = ga.g[gi - g0];
+          const int tm = g.mp / p.ts, tn = g.np / p.ts;
+          char* xin = ws + (cur ? g.off_x1 : g.off_x0);
+          char* xout = ws + (cur ? g.off_x0 : g.off_x1);
+          d.count = int(g.mats.size());
+          d.mp = g.mp; d.np = g.np;
+          d.partials = reinterpret_cast<const float*>(ws + g.off_part);
+          d.p_stride = g.npart;
+          d.npartials = g.npart;
+          d.block_base = int(blocks);
+          if (phase == 0) {
+            d.xin = xin; d.out = ws + g.off_a;
+            d.in_stride = g.x_elems; d.out_stride = g.a_elems;
+            d.tiles = tm * (tm + 1) / 2;
+          } else if (phase == 1) {
+            d.xin = ws + g.off_a; d.out = ws + g.off_b;
+            d.in_stride = g.a_elems; d.out_stride = g.a_elems;
+            d.tiles = tm * (tm + 1) / 2;
+          } else {
+            d.xin = xin; d.bop = ws + (poly ? g.off_b : g.off_a); d.out = xout;
+            d.in_stride = g.x_elems; d.b_stride = g.a_elems; d.out_stride = g.x_elems;
+            d.tiles = tm * tn;
+          }
+          blocks += int64_t(d.count) * d.tiles;
+        }
+        (void)es;
+        const int ph = phase == 0 ? MUON_PHASE_GRAM : phase == 1 ? MUON_PHASE_POLY : MUON_PHASE_APPLY;
+        probe_begin(ph, s);
+        hipError_t err = launch_gemm(phase, p.xdt, p.ts, ga, blocks, s);
+        probe_end(ph, s);
+        if (err != hipSuccess) return err;
+      }
+    }
+    cur ^= 1;
+  }
+  *final_buf = cur;
+  return hipSuccess;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+void muon_default_options(muon_options* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof(*o));
+  o->beta_slow = -1.f;
+  o->beta_ema = -1.f;
+  o->eps = 1e-7f;
+  o->ema_start = 1;
+  o->nesterov = 0;
+  o->cautious = 0;
+  o->ns_dtype = MUON_BF16;
+}
+
+const char* muon_status_str(int s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_E_NULL: return "null pointer";
+    case MUON_E_SHAPE: return "invalid shape";
+    case MUON_E_DTYPE: return "invalid element type";
+    case MUON_E_COEFFS: return "invalid coefficients or step count";
+    case MUON_E_HPARAM: return "invalid hyperparameter or option";
+    case MUON_E_WORKSPACE: return "workspace missing or too small";
+    case MUON_E_ALIAS: return "overlapping buffers";
+    case MUON_E_ALIGN: return "misaligned pointer";
+    case MUON_E_HIP: return "HIP runtime error";
+    case MUON_E_STATE: return "state inconsistent with the call";
+    default: return "unknown status";
+  }
+}
+
+size_t muon_workspace_bytes(const muon_mat* params, int32_t n, const muon_options* opt,
+                            int32_t steps) {
+  (void)steps;
+  if (n < 0 || (n > 0 && !params)) return 0;
+  const int xdt = opt ? opt->ns_dtype : MUON_BF16;
+  if (xdt != MUON_BF16 && xdt != MUON_F32) return 0;
+  std::vector<int64_t> rows(n), cols(n);
+  for (int i = 0; i < n; ++i) {
+    if (params[i].rows < 1 || params[i].cols < 1) return 0;
+    if (params[i].rows > (int64_t(1) << 30) || params[i].cols > (int64_t(1) << 30)) return 0;
+    rows[i] = params[i].rows;
+    cols[i] = params[i].cols;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  return get_plan(rows.data(), cols.data(), n, xdt).total;
+}
+
+int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, const float* coeffs,
+              int32_t steps, float lr, float wd, float beta, void* stream) {
+  if (!st) return MUON_E_NULL;
+  const int n = st->n;
+  if (n < 0) return MUON_E_SHAPE;
+  int rc;
+  if ((rc = check_coeffs(coeffs, steps)) != MUON_OK) return rc;
+  if (!finite(lr) || !finite(wd) || !(beta >= 0.f && beta < 1.f)) return MUON_E_HPARAM;
+  const muon_options& o = st->opt;
+  if ((rc = check_opt(o)) != MUON_OK) return rc;
+  const bool ema_on = o.beta_ema >= 0.f && st->step + 1 >= o.ema_start;
+  if (n == 0) {
+    st->step += 1;
+    if (ema_on) st->ema_count += 1;
+    return MUON_OK;
+  }
+  if (!params || !grads || !st->mom) return MUON_E_NULL;
+  if (o.beta_slow >= 0.f && !st->mom_slow) return MUON_E_STATE;
+  if (o.beta_ema >= 0.f && !st->ema) return MUON_E_STATE;
+  std::vector<Range> ranges;
+  std::vector<int64_t> rows(n), cols(n);
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_mat(params[i])) != MUON_OK) return rc;
+    if ((rc = check_mat(grads[i])) != MUON_OK) return rc;
+    if (grads[i].rows != params[i].rows || grads[i].cols != params[i].cols) return MUON_E_SHAPE;
+    if (!st->mom[i]) return MUON_E_STATE;
+    if (o.beta_slow >= 0.f && !st->mom_slow[i]) return MUON_E_STATE;
+    if (o.beta_ema >= 0.f && !st->ema[i]) return MUON_E_STATE;
+    const size_t dense = size_t(params[i].rows * params[i].cols);
+    const void* dps[3] = {st->mom[i], o.beta_slow >= 0.f ? st->mom_slow[i] : nullptr,
+                          o.beta_ema >= 0.f ? st->ema[i] : nullptr};
+    for (const void* q : dps)
+      if (q && reinterpret_cast<uintptr_t>(q) % 4) return MUON_E_ALIGN;
+    if (st->update_out && st->update_out[i] && reinterpret_cast<uintptr_t>(st->update_out[i]) % 4)
+      return MUON_E_ALIGN;
+    add_range(ranges, params[i].ptr, mat_bytes(params[i]));
+    add_range(ranges, grads[i].ptr, mat_bytes(grads[i]));
+    for (const void* q : dps) add_range(ranges, q, dense * 4);
+    if (st->mask_out) add_range(ranges, st->mask_out[i], dense);
+    if (st->update_out) add_range(ranges, st->update_out[i], dense * 4);
+    rows[i] = params[i].rows;
+    cols[i] = params[i].cols;
+  }
+  if (!st->workspace) return MUON_E_WORKSPACE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  const Plan& p = get_plan(rows.data(), cols.data(), n, o.ns_dtype);
+  if (st->workspace_bytes < p.total) return MUON_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(st->workspace) % kAlign) return MUON_E_ALIGN;
+  add_range(ranges, st->workspace, p.total);
+  if (overlaps(ranges)) return MUON_E_ALIAS;
+
+  // ---- descriptor table
+  char* ws = static_cast<char*>(st->workspace);
+  std::vector<MatDesc> desc(n);
+  for (int i = 0; i < n; ++i) {
+    MatDesc& d = desc[i];
+    std::memset(&d, 0, sizeof(d));
+    fill_desc(d, p, i, params[i], ws);
+    d.w = params[i].ptr; d.ldw = params[i].ld; d.wdt = params[i].dtype;
+    d.g = grads[i].ptr; d.ldg = grads[i].ld; d.gdt = grads[i].dtype;
+    d.wvec = vec_ok(d.w, d.ldw, esize(d.wdt));
+    d.gvec = vec_ok(d.g, d.ldg, esize(d.gdt));
+    d.mom = st->mom[i];
+    d.slow = o.beta_slow >= 0.f ? st->mom_slow[i] : nullptr;
+    d.ema = o.beta_ema >= 0.f ? st->ema[i] : nullptr;
+    d.mask_out = st->mask_out ? st->mask_out[i] : nullptr;
+    d.upd_out = st->update_out ? st->update_out[i] : nullptr;
+    const bool dv = (params[i].cols % 4) == 0 && reinterpret_cast<uintptr_t>(d.mom) % 16 == 0 &&
+                    (!d.slow || reinterpret_cast<uintptr_t>(d.slow) % 16 == 0) &&
+                    (!d.ema || reinterpret_cast<uintptr_t>(d.ema) % 16 == 0) &&
+                    (!d.upd_out || reinterpret_cast<uintptr_t>(d.upd_out) % 16 == 0);
+    d.dvec = dv;
+  }
+  std::vector<uint8_t> bytes;
+  table_bytes(p, desc, bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (upload_table(ws, bytes, s) != hipSuccess) return MUON_E_HIP;
+
+  ElemArgs ea;
+  std::memset(&ea, 0, sizeof(ea));
+  ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
+  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_pprefix);
+  ea.nmats = n;
+  ea.xdt = p.xdt;
+  ea.beta = beta;
+  ea.obeta = 1.0f - beta;
+  if (o.beta_slow >= 0.f) { ea.bslow = o.beta_slow; ea.obslow = 1.0f - o.beta_slow; }
+  if (o.beta_ema >= 0.f) { ea.bema = o.beta_ema; ea.obema = 1.0f - o.beta_ema; }
+  ea.lr = lr;
+  {
+    volatile float lrwd = lr * wd;   // one fp32 rounding
+    ea.lrwd = lrwd;
+  }
+  ea.eps = o.eps;
+  ea.mode = 0;
+  ea.nesterov = o.nesterov;
+  ea.cautious = o.cautious;
+  ea.use_slow = o.beta_slow >= 0.f;
+  ea.ema_on = ema_on;
+  ea.ema_first = ema_on && st->ema_count == 0;
+  ea.scale_o = steps == 0;
+
+  probe_begin(MUON_PHASE_PREPARE, s);
+  hipError_t err = launch_prepare(ea, p.pprefix[n], s);
+  probe_end(MUON_PHASE_PREPARE, s);
+  if (err != hipSuccess) return MUON_E_HIP;
+  int fb = 0;
+  if (run_ns(p, ws, coeffs, steps, o.eps, s, &fb) != hipSuccess) return MUON_E_HIP;
+  ea.final_buf = fb;
+  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+  probe_begin(MUON_PHASE_FINISH, s);
+  err = launch_finish(ea, p.fprefix[n], s);
+  probe_end(MUON_PHASE_FINISH, s);
+  if (err != hipSuccess) return MUON_E_HIP;
+  st->step += 1;
+  if (ema_on) st->ema_count += 1;
+  return MUON_OK;
+}
+
+int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const float* coeffs,
+                       int32_t steps, const muon_options* opt, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (n < 0) return MUON_E_SHAPE;
+  int rc;
+  if ((rc = check_coeffs(coeffs, steps)) != MUON_OK) return rc;
+  muon_options o;
+  muon_default_options(&o);
+  if (opt) {
+    o.eps = opt->eps;
+    o.ns_dtype = opt->ns_dtype;
+  }
+  if ((rc = check_opt(o)) != MUON_OK) return rc;
+  if (n == 0) return MUON_OK;
+  if (!in || !out) return MUON_E_NULL;
+  std::vector<Range> ranges;
+  std::vector<int64_t> rows(n), cols(n);
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_mat(in[i])) != MUON_OK) return rc;
+    if ((rc = check_mat(out[i])) != MUON_OK) return rc;
+    if (in[i].rows != out[i].rows || in[i].cols != out[i].cols) return MUON_E_SHAPE;
+    add_range(ranges, in[i].ptr, mat_bytes(in[i]));
+    add_range(ranges, out[i].ptr, mat_bytes(out[i]));
+    rows[i] = in[i].rows;
+    cols[i] = in[i].cols;
+  }
+  if (!workspace) return MUON_E_WORKSPACE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  const Plan& p = get_plan(rows.data(), cols.data(), n, o.ns_dtype);
+  if (workspace_bytes < p.total) return MUON_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MUON_E_ALIGN;
+  add_range(ranges, workspace, p.total);
+  if (overlaps(ranges)) return MUON_E_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  std::vector<MatDesc> desc(n);
+  for (int i = 0; i < n; ++i) {
+    MatDesc& d = desc[i];
+    std::memset(&d, 0, sizeof(d));
+    fill_desc(d, p, i, in[i], ws);
+    d.g = in[i].ptr; d.ldg = in[i].ld; d.gdt = in[i].dtype;
+    d.w = out[i].ptr; d.ldw = out[i].ld; d.wdt = out[i].dtype;
+    d.gvec = vec_ok(d.g, d.ldg, esize(d.gdt));
+    d.wvec = vec_ok(d.w, d.ldw, esize(d.wdt));
+    d.dvec = 0;
+  }
+  std::vector<uint8_t> bytes;
+  table_bytes(p, desc, bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (upload_table(ws, bytes, s) != hipSuccess) return MUON_E_HIP;
+  ElemArgs ea;
+  std::memset(&ea, 0, sizeof(ea));
+  ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
+  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_pprefix);
+  ea.nmats = n;
+  ea.xdt = p.xdt;
+  ea.eps = o.eps;
+  ea.mode = 1;
+  ea.scale_o = steps == 0;
+  probe_begin(MUON_PHASE_PREPARE, s);
+  hipError_t err = launch_prepare(ea, p.pprefix[n], s);
+  probe_end(MUON_PHASE_PREPARE, s);
+  if (err != hipSuccess) return MUON_E_HIP;
+  int fb = 0;
+  if (run_ns(p, ws, coeffs, steps, o.eps, s, &fb) != hipSuccess) return MUON_E_HIP;
+  ea.final_buf = fb;
+  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+  probe_begin(MUON_PHASE_FINISH, s);
+  err = launch_finish(ea, p.fprefix[n], s);
+  probe_end(MUON_PHASE_FINISH, s);
+  return err == hipSuccess ? MUON_OK : MUON_E_HIP;
+}
+
+int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state* st,
+                   float w_final, void* stream) {
+  if (!st) return MUON_E_NULL;
+  const int n = st->n;
+  if (n < 0) return MUON_E_SHAPE;
+  if (!(w_final >= 0.f && w_final <= 1.f)) return MUON_E_HPARAM;
+  if (n == 0) return MUON_OK;
+  if (!out || !params) return MUON_E_NULL;
+  if (!st->ema) return MUON_E_STATE;
+  int rc;
+  std::vector<Range> ranges;
+  std::vector<int64_t> rows(n), cols(n);
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_mat(out[i])) != MUON_OK) return rc;
+    if ((rc = check_mat(params[i])) != MUON_OK) return rc;
+    if (out[i].rows != params[i].rows || out[i].cols != params[i].cols) return MUON_E_SHAPE;
+    if (!st->ema[i]) return MUON_E_STATE;
+    if (reinterpret_cast<uintptr_t>(st->ema[i]) % 4) return MUON_E_ALIGN;
+    const bool same = out[i].ptr == params[i].ptr && out[i].ld == params[i].ld &&
+                      out[i].dtype == params[i].dtype;
+    add_range(ranges, out[i].ptr, mat_bytes(out[i]));
+    if (!same) add_range(ranges, params[i].ptr, mat_bytes(params[i]));
+    add_range(ranges, st->ema[i], size_t(out[i].rows * out[i].cols) * 4);
+    rows[i] = out[i].rows;
+    cols[i] = out[i].cols;
+  }
+  if (!st->workspace) return MUON_E_WORKSPACE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  const Plan& p = get_plan(rows.data(), cols.data(), n, st->opt.ns_dtype == MUON_F32 ? MUON_F32 : MUON_BF16);
+  if (st->workspace_bytes < p.total) return MUON_E_WORKSPACE;
+  add_range(ranges, st->workspace, p.total);
+  if (overlaps(ranges)) return MUON_E_ALIAS;
+  char* ws = static_cast<char*>(st->workspace);
+  std::vector<MatDesc> desc(n);
+  for (int i = 0; i < n; ++i) {
+    MatDesc& d = desc[i];
+    std::memset(&d, 0, sizeof(d));
+    fill_desc(d, p, i, out[i], ws);
+    d.w = out[i].ptr; d.ldw = out[i].ld; d.wdt = out[i].dtype;
+    d.g = params[i].ptr; d.ldg = params[i].ld; d.gdt = params[i].dtype;
+    d.wvec = vec_ok(d.w, d.ldw, esize(d.wdt));
+    d.gvec = vec_ok(d.g, d.ldg, esize(d.gdt));
+    d.ema = st->ema[i];
+    d.dvec = (out[i].cols % 4) == 0 && reinterpret_cast<uintptr_t>(d.ema) % 16 == 0;
+  }
+  std::vector<uint8_t> bytes;
+  table_bytes(p, desc, bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (upload_table(ws, bytes, s) != hipSuccess) return MUON_E_HIP;
+  ElemArgs ea;
+  std::memset(&ea, 0, sizeof(ea));
+  ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
+  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+  ea.nmats = n;
+  const float wf = w_final;
+  volatile float owf = 1.0f - wf;
+  return launch_blend(ea, p.fprefix[n], wf, owf, s) == hipSuccess ? MUON_OK : MUON_E_HIP;
+}
+
+int muon_probe_arm(int32_t phase, int32_t capacity) {
+  if (phase < 0 || phase > 4 || capacity < 1 || capacity > 65536) return MUON_E_HPARAM;
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto e : g_probe.ev0) (void)hipEventDestroy(e);
+  for (auto e : g_probe.ev1) (void)hipEventDestroy(e);
+  g_probe = Probe();
+  g_probe.ev0.resize(capacity);
+  g_probe.ev1.resize(capacity);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&g_probe.ev0[i]) != hipSuccess || hipEventCreate(&g_probe.ev1[i]) != hipSuccess)
+      return MUON_E_HIP;
+  }
+  g_probe.cap = capacity;
+  g_probe.phase = phase;
+  return MUON_OK;
+}
+
+int muon_probe_read(float* ms, int32_t capacity, int32_t* count) {
+  if (!ms || !count) return MUON_E_NULL;
+  std::lock_guard<std::mutex> lk(g_mu);
+  const int k = std::min(capacity, g_probe.used);
+  for (int i = 0; i < k; ++i) {
+    if (hipEventSynchronize(g_probe.ev1[i]) != hipSuccess) return MUON_E_HIP;
+    if (hipEventElapsedTime(&ms[i], g_probe.ev0[i], g_probe.ev1[i]) != hipSuccess) return MUON_E_HIP;
+  }
+  *count = k;
+  return MUON_OK;
+}
+
+int muon_probe_disarm(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto e : g_probe.ev0) (void)hipEventDestroy(e);
+  for (auto e : g_probe.ev1) (void)hipEventDestroy(e);
+  g_probe = Probe();
+  return MUON_OK;
+}
+
+int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt, int32_t steps,
+                   const float* coeffs, int32_t* n_groups, int32_t* tiles, int32_t cap,
+                   int32_t* launches_per_step) {
+  if (n < 0 || steps < 0 || steps > MUON_MAX_STEPS) return MUON_E_SHAPE;
+  if (n > 0 && !params) return MUON_E_NULL;
+  const int xdt = opt ? opt->ns_dtype : MUON_BF16;
+  if (xdt != MUON_BF16 && xdt != MUON_F32) return MUON_E_DTYPE;
+  std::vector<int64_t> rows(n), cols(n);
+  for (int i = 0; i < n; ++i) {
+    if (params[i].rows < 1 || params[i].cols < 1) return MUON_E_SHAPE;
+    rows[i] = params[i].rows;
+    cols[i] = params[i].cols;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  const Plan& p = get_plan(rows.data(), cols.data(), n, xdt);
+  if (n_groups) *n_groups = int(p.groups.size());
+  if (tiles)
+    for (int i = 0; i < std::min<int>(cap, int(p.groups.size())); ++i) tiles[i] = p.ts;
+  if (launches_per_step) {
+    const int sets = int((p.groups.size() + kMaxGroups - 1) / kMaxGroups);
+    int l = n > 0 ? 2 : 0;
+    for (int j = 0; j < steps && n > 0; ++j) {
+      const bool poly = !coeffs || coeffs[3 * j + 2] != 0.f;
+      l += sets * (poly ? 3 : 2);
+    }
+    *launches_per_step = l;
+  }
+  return MUON_OK;
+}
+
+}  // extern "C"

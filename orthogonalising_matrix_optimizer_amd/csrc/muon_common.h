@@ -1,0 +1,105 @@
+// Shared host/device definitions of the Muon step library (gfx950).
+//
+// Data layout in the caller's workspace (all offsets 256-byte aligned):
+//   * per matrix, the Newton-Schulz iterate X in its wide orientation
+//     (m = min(rows, cols), n = max(rows, cols)), zero-padded to mp x np with
+//     mp, np multiples of the group's tile edge, row-major, ld = np; two such
+//     buffers (ping-pong);
+//   * per matrix, the m x m Gram matrix A and polynomial B, padded to mp x mp;
+//   * per matrix, one fp32 partial sum of squares per 64x64 prepare tile;
+//   * the device descriptor table (MatDesc[n]) and tile prefix sums.
+// Zero padding stays zero through every product (zero rows and columns of X
+// give zero rows and columns of A, B and the next X), so the GEMM kernels run
+// on full tiles only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kThreads = 256;     // threads per block, every kernel
+constexpr int kEw = 64;           // edge of the elementwise (prepare/finish) tiles
+constexpr int kMaxGroups = 8;     // effective-shape groups per grouped launch
+
+enum ElemType : int32_t { kBF16 = 0, kF32 = 1 };
+
+// Per-matrix descriptor, resident in the workspace.
+struct MatDesc {
+  void* w;              // parameters (rows x cols, ldw)
+  const void* g;        // gradient (rows x cols, ldg); input matrix for orthogonalize
+  float* mom;           // momentum, dense rows x cols
+  float* slow;          // slow momentum or null
+  float* ema;           // weight average or null
+  uint8_t* mask_out;    // diagnostic or null
+  float* upd_out;       // diagnostic or null
+  void* x0;             // ping-pong iterate buffers (mp x np, ld np)
+  void* x1;
+  float* partials;      // prepare-tile partial sums of squares
+  int64_t ldw, ldg;
+  int32_t rows, cols;   // source shape
+  int32_t mp, np;       // padded effective shape
+  int32_t tall;         // rows > cols: X = U^T
+  int32_t wdt, gdt;     // element types of w and g
+  int32_t wvec, gvec;   // 16-byte vector access allowed on w / g rows
+  int32_t dvec;         // dense fp32 rows (mom, slow, ema, upd) allow float4 access
+  int32_t npartials;
+  int32_t _pad;
+};
+
+// Kernel arguments of the elementwise kernels.
+struct ElemArgs {
+  const MatDesc* mats;
+  const int64_t* prefix;   // block prefix sums per matrix (n + 1 entries)
+  int32_t nmats;
+  int32_t xdt;             // element type of the iterate
+  float beta, obeta;       // momentum and (1 - beta), fp32
+  float bslow, obslow;     // slow momentum and (1 - beta_slow)
+  float bema, obema;       // weight average and (1 - beta_ema)
+  float lr, lrwd;          // lr and fl(lr * wd)
+  float eps;
+  int32_t mode;            // prepare: 0 step, 1 copy; finish: 0 step, 1 write O
+  int32_t nesterov, cautious, use_slow;
+  int32_t ema_on, ema_first;
+  int32_t final_buf;       // iterate buffer holding O (0 -> x0, 1 -> x1)
+  int32_t scale_o;         // steps == 0: O = s * X0
+};
+
+// One effective-shape group inside a grouped GEMM launch.
+struct GemmGroup {
+  const void* xin;        // GRAM: X; POLY: A; APPLY: X
+  const void* bop;        // APPLY: B (or A for a cubic step); otherwise unused
+  void* out;              // GRAM: A; POLY: B; APPLY: next X
+  const float* partials;  // first iteration: per-matrix norm partials
+  int64_t in_stride;      // elements between consecutive matrices of xin
+  int64_t b_stride;       // ... of bop
+  int64_t out_stride;     // ... of out
+  int64_t p_stride;       // floats between consecutive matrices' partials
+  int32_t count;          // matrices in the group
+  int32_t mp, np;
+  int32_t tiles;          // tiles per matrix
+  int32_t block_base;     // first block of this group in the launch
+  int32_t npartials;
+};
+
+struct GemmArgs {
+  GemmGroup g[kMaxGroups];
+  int32_t ngroups;
+  int32_t first;          // first iteration: fold the norm scale s in
+  float ca, cb, cc;       // coefficients of this iteration
+  float cbb;              // APPLY: multiplier of the product (1, or b when B = bA)
+  float eps;
+  int32_t _pad;
+};
+
+}  // namespace muon
+
+// Launchers (defined in the .hip sources; called by the C ABI layer).
+namespace muon {
+hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s);
+hipError_t launch_finish(const ElemArgs& a, int64_t blocks, hipStream_t s);
+hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,
+                        hipStream_t s);
+// phase: 0 GRAM, 1 POLY, 2 APPLY; ts: tile edge (64, 128, 256).
+hipError_t launch_gemm(int phase, int xdt, int ts, const GemmArgs& a,
+                       int64_t blocks, hipStream_t s);
+}  // namespace muon

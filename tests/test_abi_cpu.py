@@ -1,0 +1,271 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+declared in include/muon.h, agrees with the header on struct layout, and
+rejects bad arguments before touching the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from orthogonalising_matrix_optimizer_amd import _lib
+from workloads import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from orthogonalising_matrix_optimizer_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert "muon_step" in names and "muon_orthogonalize" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (muon_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c_compiler():
+    prog = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "muon.h"
+#define O(T, f) printf(#T "." #f " %zu\n", offsetof(T, f))
+int main(void) {
+  printf("muon_mat %zu\nmuon_options %zu\nmuon_state %zu\n", sizeof(muon_mat),
+         sizeof(muon_options), sizeof(muon_state));
+  O(muon_mat, ptr); O(muon_mat, rows); O(muon_mat, cols); O(muon_mat, ld); O(muon_mat, dtype);
+  O(muon_options, beta_slow); O(muon_options, beta_ema); O(muon_options, eps);
+  O(muon_options, nesterov); O(muon_options, ema_start); O(muon_options, cautious);
+  O(muon_options, ns_dtype);
+  O(muon_state, n); O(muon_state, mom); O(muon_state, mom_slow); O(muon_state, ema);
+  O(muon_state, mask_out); O(muon_state, update_out); O(muon_state, workspace);
+  O(muon_state, workspace_bytes); O(muon_state, step); O(muon_state, ema_count);
+  O(muon_state, opt);
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        open(c, "w").write(prog)
+        exe = os.path.join(d, "layout")
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(l.split() for l in lines if l.strip())
+    ct = {"muon_mat": _lib.MuonMat, "muon_options": _lib.MuonOptions, "muon_state": _lib.MuonState}
+    for k, v in got.items():
+        if "." in k:
+            s, f = k.split(".")
+            assert getattr(ct[s], f).offset == int(v), k
+        else:
+            assert ctypes.sizeof(ct[k]) == int(v), k
+
+
+def test_status_strings(lib):
+    for code in _lib.STATUS:
+        assert lib.muon_status_str(code)
+    assert lib.muon_status_str(0) == b"ok"
+
+
+# ---------------------------------------------------------------- validation
+BASE = 0x7f0000000000   # fake device addresses: validation fails before any use
+
+
+def _setup(lib, shapes, dtype=_lib.MUON_BF16, ws_bytes=None, **opt_kw):
+    n = len(shapes)
+    addr = [BASE]
+
+    def take(nbytes):
+        a = addr[0]
+        addr[0] += (nbytes + 4095) // 4096 * 4096 + 4096
+        return a
+
+    es = 2 if dtype == _lib.MUON_BF16 else 4
+    params = _lib.mat_array((take(r * c * es), r, c, c, dtype) for r, c in shapes)
+    grads = _lib.mat_array((take(r * c * es), r, c, c, dtype) for r, c in shapes)
+    mom = _lib.ptr_array(take(r * c * 4) for r, c in shapes)
+    opt = _lib.default_options()
+    for k, v in opt_kw.items():
+        setattr(opt, k, v)
+    need = lib.muon_workspace_bytes(params, n, opt, 5)
+    st = _lib.MuonState()
+    st.n = n
+    st.mom = ctypes.cast(mom, ctypes.POINTER(ctypes.c_void_p))
+    st.workspace = take(need)
+    st.workspace_bytes = need if ws_bytes is None else ws_bytes
+    st.opt = opt
+    keep = [params, grads, mom]
+    return params, grads, st, keep
+
+
+def _coeffs(k=5):
+    return _lib.float_array(np.array([gen.QUINTIC] * k).ravel())
+
+
+def _step(lib, params, grads, st, coeffs=None, steps=5, lr=0.02, wd=0.0, beta=0.95):
+    return lib.muon_step(params, grads, st if st is not None else None,
+                         coeffs if coeffs is not None else _coeffs(steps), steps, lr, wd, beta,
+                         None)
+
+
+E = _lib.CODES
+
+
+def test_rejects_bad_scalars(lib):
+    p, g, st, keep = _setup(lib, [(8, 16), (16, 8)])
+    assert lib.muon_step(p, g, None, _coeffs(), 5, 0.02, 0.0, 0.95, None) == E["MUON_E_NULL"]
+    assert _step(lib, p, g, st, steps=17, coeffs=_coeffs(17)) == E["MUON_E_COEFFS"]
+    assert lib.muon_step(p, g, st, _coeffs(), -1, 0.02, 0.0, 0.95, None) == E["MUON_E_COEFFS"]
+    bad = _lib.float_array([1.0, float("nan"), 0.0] * 5)
+    assert _step(lib, p, g, st, coeffs=bad) == E["MUON_E_COEFFS"]
+    assert lib.muon_step(p, g, st, None, 5, 0.02, 0.0, 0.95, None) == E["MUON_E_NULL"]
+    assert _step(lib, p, g, st, lr=float("inf")) == E["MUON_E_HPARAM"]
+    assert _step(lib, p, g, st, wd=float("nan")) == E["MUON_E_HPARAM"]
+    assert _step(lib, p, g, st, beta=1.0) == E["MUON_E_HPARAM"]
+    assert _step(lib, p, g, st, beta=-0.1) == E["MUON_E_HPARAM"]
+    assert st.step == 0 and st.ema_count == 0
+
+
+def test_rejects_bad_options(lib):
+    p, g, st, keep = _setup(lib, [(8, 16)])
+    for field, val, code in [("eps", float("nan"), "MUON_E_HPARAM"), ("eps", -1.0, "MUON_E_HPARAM"),
+                             ("ns_dtype", 7, "MUON_E_DTYPE"), ("beta_slow", 1.0, "MUON_E_HPARAM"),
+                             ("beta_ema", 2.0, "MUON_E_HPARAM"), ("cautious", 1, "MUON_E_HPARAM"),
+                             ("nesterov", 3, "MUON_E_HPARAM")]:
+        o = _lib.default_options()
+        setattr(o, field, val)
+        st.opt = o
+        assert _step(lib, p, g, st) == E[code], field
+    assert st.step == 0
+
+
+def test_rejects_bad_matrices(lib):
+    p, g, st, keep = _setup(lib, [(8, 16), (16, 8)])
+    good = (p[1].ptr, p[1].rows, p[1].cols, p[1].ld, p[1].dtype)
+    for (r, c, ld, dt, code) in [(0, 8, 8, 0, "MUON_E_SHAPE"), (16, 8, 4, 0, "MUON_E_SHAPE"),
+                                 (16, 8, 8, 5, "MUON_E_DTYPE")]:
+        p[1] = _lib.MuonMat(good[0], r, c, ld, dt, 0)
+        assert _step(lib, p, g, st) == E[code]
+    p[1] = _lib.MuonMat(good[0] + 1, 16, 8, 8, _lib.MUON_BF16, 0)
+    assert _step(lib, p, g, st) == E["MUON_E_ALIGN"]
+    p[1] = _lib.MuonMat(None, 16, 8, 8, _lib.MUON_BF16, 0)
+    assert _step(lib, p, g, st) == E["MUON_E_NULL"]
+    p[1] = _lib.MuonMat(*good, 0)
+    g[1] = _lib.MuonMat(g[1].ptr, 8, 16, 16, _lib.MUON_BF16, 0)
+    assert _step(lib, p, g, st) == E["MUON_E_SHAPE"]
+    assert st.step == 0
+
+
+def test_rejects_missing_state(lib):
+    p, g, st, keep = _setup(lib, [(8, 16)], beta_slow=0.99)
+    assert _step(lib, p, g, st) == E["MUON_E_STATE"]        # slow momentum missing
+    p, g, st, keep = _setup(lib, [(8, 16)], beta_ema=0.99)
+    assert _step(lib, p, g, st) == E["MUON_E_STATE"]        # average missing
+    p, g, st, keep = _setup(lib, [(8, 16)])
+    st.mom = None
+    assert _step(lib, p, g, st) == E["MUON_E_NULL"]
+
+
+def test_rejects_workspace_and_aliasing(lib):
+    p, g, st, keep = _setup(lib, [(8, 16), (16, 8)])
+    need = st.workspace_bytes
+    st.workspace_bytes = need - 1
+    assert _step(lib, p, g, st) == E["MUON_E_WORKSPACE"]
+    st.workspace_bytes = need
+    ws = st.workspace
+    st.workspace = None
+    assert _step(lib, p, g, st) == E["MUON_E_WORKSPACE"]
+    st.workspace = ws + 16
+    assert _step(lib, p, g, st) == E["MUON_E_ALIGN"]
+    st.workspace = ws
+    g0 = g[0]
+    g[0] = _lib.MuonMat(p[0].ptr + 64, g0.rows, g0.cols, g0.ld, g0.dtype, 0)   # overlaps params[0]
+    assert _step(lib, p, g, st) == E["MUON_E_ALIAS"]
+    g[0] = g0
+    st.mom[1] = p[1].ptr                                                      # momentum over params
+    assert _step(lib, p, g, st) == E["MUON_E_ALIAS"]
+    st.mom[1] = ws + 1024                                                     # momentum in workspace
+    assert _step(lib, p, g, st) == E["MUON_E_ALIAS"]
+    assert st.step == 0 and st.ema_count == 0
+
+
+def test_empty_step_only_advances_counters(lib):
+    st = _lib.MuonState()
+    st.n = 0
+    st.opt = _lib.default_options()
+    st.opt.beta_ema = 0.9
+    st.opt.ema_start = 2
+    for t in range(1, 4):
+        assert lib.muon_step(None, None, st, _coeffs(), 5, 0.02, 0.0, 0.95, None) == 0
+        assert st.step == t and st.ema_count == max(0, t - 1)
+
+
+def test_orthogonalize_and_blend_validation(lib):
+    p, g, st, keep = _setup(lib, [(8, 16), (16, 8)])
+    opt = _lib.default_options()
+    need = lib.muon_workspace_bytes(p, 2, opt, 5)
+    assert lib.muon_orthogonalize(p, g, 2, _coeffs(), 5, opt, st.workspace, need - 256, None) == \
+        E["MUON_E_WORKSPACE"]
+    g[1] = _lib.MuonMat(g[1].ptr, 8, 16, 16, _lib.MUON_BF16, 0)
+    assert lib.muon_orthogonalize(p, g, 2, _coeffs(), 5, opt, st.workspace, need, None) == \
+        E["MUON_E_SHAPE"]
+    assert lib.muon_orthogonalize(p, p, 1, _coeffs(), 5, opt, st.workspace, need, None) == \
+        E["MUON_E_ALIAS"]
+    assert lib.muon_orthogonalize(p, g, 0, _coeffs(), 5, opt, st.workspace, need, None) == 0
+    assert lib.muon_ema_blend(p, p, st, 0.35, None) == E["MUON_E_STATE"]
+    assert lib.muon_ema_blend(p, p, st, 1.5, None) == E["MUON_E_HPARAM"]
+    assert lib.muon_probe_arm(9, 4) == E["MUON_E_HPARAM"]
+    assert lib.muon_probe_arm(1, 0) == E["MUON_E_HPARAM"]
+
+
+# ---------------------------------------------------------------- planning
+def _plan(lib, shapes, steps=5, coeffs=None, ns=_lib.MUON_BF16):
+    mats = _lib.mat_array((0, r, c, c, 0) for r, c in shapes)
+    opt = _lib.default_options()
+    opt.ns_dtype = ns
+    ng, lps = ctypes.c_int32(), ctypes.c_int32()
+    tiles = (ctypes.c_int32 * 16)()
+    c = _lib.float_array(np.array(coeffs if coeffs is not None else [gen.QUINTIC] * steps).ravel())
+    assert lib.muon_plan_info(mats, len(shapes), opt, steps, c, ctypes.byref(ng), tiles, 16,
+                              ctypes.byref(lps)) == 0
+    return ng.value, tiles[0], lps.value, lib.muon_workspace_bytes(mats, len(shapes), opt, steps)
+
+
+def test_plan_groups_and_launches(lib):
+    shapes = gen.gpt124m_shapes()
+    ng, ts, lps, ws = _plan(lib, shapes)
+    assert ng == 2 and ts == 256
+    assert lps == 2 + 5 * 3                       # prepare, 5 x (gram, poly, apply), finish
+    assert _plan(lib, shapes, coeffs=[gen.CUBIC] * 5)[2] == 2 + 5 * 2
+    # iterate ping-pong + Gram + polynomial buffers for 48 (768,768) and 24 (768,3072)
+    floor = 2 * (48 * (2 * 768 * 768 + 2 * 768 * 768) + 24 * (2 * 768 * 3072 + 2 * 768 * 768))
+    assert floor <= ws <= floor * 1.01
+    assert ws % 256 == 0
+    ng, ts, lps, ws32 = _plan(lib, [(256, 512)], ns=_lib.MUON_F32)
+    assert ng == 1 and ts == 64            # one small matrix: smallest tiles
+    assert ws32 >= 4 * (2 * 256 * 512 + 2 * 256 * 256)
+    assert _plan(lib, gen.moe_share_shapes())[0] == 2
+    assert _plan(lib, [(5, 3), (3, 5), (7, 7)])[0] == 2
+
+
+def test_workspace_bytes_rejects_bad_shapes(lib):
+    mats = _lib.mat_array([(0, 0, 5, 5, 0)])
+    assert lib.muon_workspace_bytes(mats, 1, None, 5) == 0
+    assert lib.muon_workspace_bytes(None, -1, None, 5) == 0

@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle, through the C ABI."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import orthogonalising_matrix_optimizer_amd as mo
+from oracle import muon_oracle as orc
+from tests.gpu_helpers import (TOL_BF16, TOL_F32, TOL_SIGMA, announce, dev_bf16, dev_f32, host,
+                               sigma_dev)
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mo._lib.load()
+
+
+@pytest.fixture
+def tile(request):
+    """Force a Newton-Schulz tile edge for the duration of a test."""
+    old = os.environ.get("MUON_TILE")
+    val = getattr(request, "param", None)
+    if val:
+        os.environ["MUON_TILE"] = str(val)
+    yield val
+    if old is None:
+        os.environ.pop("MUON_TILE", None)
+    else:
+        os.environ["MUON_TILE"] = old
+
+
+def _table(kind, k):
+    return gen.coeff_table(kind, k)
+
+
+def _ortho(us, kind, k, ns, out_dtype=torch.float32, eps=1e-7):
+    ins = [dev_f32(u) if u.dtype == np.float32 else dev_bf16(u) for u in us]
+    outs = [torch.empty(t.shape, dtype=out_dtype, device="cuda") for t in ins]
+    mo.orthogonalize(ins, outs, coeffs=_table(kind, k), steps=k, ns_dtype=ns, eps=eps)
+    torch.cuda.synchronize()
+    return [host(o) for o in outs]
+
+
+# ------------------------------------------------------------ orthogonalize
+@pytest.mark.parametrize("kind", ["cubic", "quintic"])
+@pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
+def test_single_matrix_256x512(kind, ns, tol):
+    announce(f"orthogonalize 256x512 {kind} {ns}")
+    G = gen.grad_matrix(256, 512, 0, 0, 0).astype(np.float32)
+    (O,) = _ortho([G], kind, 5, ns)
+    ref = orc.orthogonalize(G.astype(np.float64), _table(kind, 5))
+    assert orc.rel_fro(O, ref) <= tol
+    assert sigma_dev(O, ref) <= TOL_SIGMA
+
+
+RAGGED = [(200, 333), (333, 200), (7, 11), (11, 7), (1, 5), (5, 1), (300, 300), (64, 1000),
+          (1000, 70), (200, 333), (129, 65)]
+
+
+@pytest.mark.parametrize("tile", [64, 128, 256], indirect=True)
+@pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
+def test_ragged_mixed_shapes(tile, ns, tol):
+    announce(f"orthogonalize ragged tile={tile} {ns}")
+    us = [gen.grad_matrix(r, c, 1, 0, i).astype(np.float32) for i, (r, c) in enumerate(RAGGED)]
+    outs = _ortho(us, "quintic", 5, ns)
+    for u, o in zip(us, outs):
+        ref = orc.orthogonalize(u.astype(np.float64), _table("quintic", 5))
+        # a 1-row or 1-column matrix has one singular value; bf16 rounding of a
+        # near-unit vector stays well inside the tolerance
+        assert orc.rel_fro(o, ref) <= tol, u.shape
+        assert sigma_dev(o, ref) <= TOL_SIGMA, u.shape
+
+
+def test_bf16_inputs_and_outputs():
+    announce("orthogonalize bf16 in/out")
+    shapes = [(96, 160), (160, 96), (128, 128)]
+    us = [gen.bf16_bits_from_f32(gen.grad_matrix(r, c, 2, 0, i).astype(np.float32) * 1e-3)
+          for i, (r, c) in enumerate(shapes)]
+    outs = _ortho(us, "quintic", 6, "bf16", out_dtype=torch.bfloat16)
+    for u, o in zip(us, outs):
+        ref = orc.orthogonalize(gen.f32_from_bf16_bits(u).astype(np.float64), _table("quintic", 6))
+        assert orc.rel_fro(o, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("ns,tol", [("f32", 1e-6), ("bf16", 5e-3)])
+def test_zero_steps_is_normalisation(ns, tol):
+    announce(f"orthogonalize steps=0 {ns}")
+    us = [gen.grad_matrix(r, c, 3, 0, i).astype(np.float32) for i, (r, c) in
+          enumerate([(40, 72), (72, 40)])]
+    outs = _ortho(us, "quintic", 0, ns)
+    for u, o in zip(us, outs):
+        ref = u.astype(np.float64) / (np.linalg.norm(u.astype(np.float64)) + 1e-7)
+        assert orc.rel_fro(o, ref) <= tol
+
+
+def test_cubic_converges_to_polar_factor():
+    announce("orthogonalize cubic polar")
+    rng = np.random.default_rng(11)
+    P, _ = np.linalg.qr(rng.standard_normal((64, 64)))
+    Q, _ = np.linalg.qr(rng.standard_normal((96, 64)))
+    U = (P @ np.diag(np.linspace(1.0, 3.0, 64)) @ Q.T).astype(np.float32)
+    (O,) = _ortho([U], "cubic", 16, "f32")
+    Pu, _, Qt = np.linalg.svd(U.astype(np.float64), full_matrices=False)
+    assert np.linalg.norm(O - Pu @ Qt) / np.sqrt(64) < 1e-4
+
+
+def test_zero_matrix_gives_zero():
+    announce("orthogonalize zero")
+    (O,) = _ortho([np.zeros((33, 70), np.float32)], "quintic", 5, "bf16")
+    assert np.all(O == 0)
+
+
+# ------------------------------------------------------------ full step
+def _make(shapes, dtype, seed=0, rms=1e-3):
+    gs, ws = [], []
+    for i, (r, c) in enumerate(shapes):
+        g = gen.grad_matrix(r, c, seed, 0, i, rms).astype(np.float32)
+        w = gen.param_matrix(r, c, seed, i).astype(np.float32)
+        if dtype == "bf16":
+            gs.append(gen.bf16_bits_from_f32(g))
+            ws.append(gen.bf16_bits_from_f32(w))
+        else:
+            gs.append(g)
+            ws.append(w)
+    return gs, ws
+
+
+def _dev(a):
+    return dev_bf16(a) if a.dtype == np.uint16 else dev_f32(a)
+
+
+def _val(a):
+    return gen.f32_from_bf16_bits(a) if a.dtype == np.uint16 else a
+
+
+@pytest.mark.parametrize("dtype,ns", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_step_matches_oracle(dtype, ns):
+    announce(f"step {dtype} ns={ns}")
+    shapes = [(256, 512), (512, 256), (200, 333), (64, 64)]
+    gs, ws = _make(shapes, dtype, rms=None if dtype == "f32" else 1e-3)
+    params = [_dev(w) for w in ws]
+    grads = [_dev(g) for g in gs]
+    lr, wd, beta = 0.02, 0.1, 0.95
+    opt = mo.Muon(params, lr=lr, wd=wd, beta=beta, steps=5, coeffs="quintic", ns_dtype=ns,
+                  diagnostics=True)
+    opt.step(grads)
+    torch.cuda.synchronize()
+    st = orc.OracleState(shapes)
+    w0 = [_val(w).astype(np.float64) for w in ws]
+    ref = orc.muon_step(w0, [_val(g) for g in gs], st, _table("quintic", 5), lr, wd, beta,
+                        param_dtype=dtype)
+    tol = TOL_F32 if ns == "f32" else TOL_BF16
+    for i in range(len(shapes)):
+        np.testing.assert_array_equal(host(opt.mom[i]), st.mom[i])
+        O = host(opt.update[i])
+        assert orc.rel_fro(O, ref["O"][i]) <= tol, shapes[i]
+        assert sigma_dev(O, ref["O"][i]) <= TOL_SIGMA
+        want = orc.store(orc.update_f32(w0[i], O, lr, wd), dtype)
+        np.testing.assert_array_equal(host(params[i]).astype(np.float64), want)
+        assert np.all(host(opt.mask[i]) == 1)
+        # free-running: within one storage ulp plus lr times the O deviation
+        w = host(params[i]).astype(np.float64)
+        wr = ref["params"][i]
+        ulp = np.spacing(np.abs(wr).astype(np.float32)).astype(np.float64) * (
+            2 ** 16 if dtype == "bf16" else 1)
+        dev = np.abs(O - ref["O"][i])
+        assert np.all(np.abs(w - wr) <= ulp + lr * dev + 1e-12)
+    assert opt.step_count == 1
+
+
+def test_anvil_ten_steps_state_forced():
+    """Fast/slow momentum, six map steps, cautious decay, EMA: at every step the
+    oracle starts from the GPU's stored state and must agree exactly on the
+    state, the mask and the update arithmetic, and within tolerance on O."""
+    announce("anvil 10 steps")
+    shapes = [(128, 256), (256, 128), (96, 96), (100, 37)]
+    _, ws = _make(shapes, "bf16")
+    params = [_dev(w) for w in ws]
+    lr, wd, beta, bs, be = 0.02, 0.1, 0.9, 0.99, 0.99
+    opt = mo.Muon(params, lr=lr, wd=wd, beta=beta, steps=6, coeffs="quintic", beta_slow=bs,
+                  beta_ema=be, ema_start=1, cautious=True, diagnostics=True)
+    coeffs = _table("quintic", 6)
+    M = [np.zeros(s, np.float32) for s in shapes]
+    S = [np.zeros(s, np.float32) for s in shapes]
+    E = [np.zeros(s, np.float32) for s in shapes]
+    W = [_val(w) for w in ws]
+    for t in range(1, 11):
+        gs = [gen.bf16_bits_from_f32(gen.grad_matrix(r, c, 0, t, i, 1e-3).astype(np.float32))
+              for i, (r, c) in enumerate(shapes)]
+        opt.step([_dev(g) for g in gs])
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            g = _val(gs[i])
+            M[i] = orc.momentum_f32(M[i], g, beta)
+            S[i] = orc.momentum_f32(S[i], g, bs)
+            np.testing.assert_array_equal(host(opt.mom[i]), M[i])
+            np.testing.assert_array_equal(host(opt.mom_slow[i]), S[i])
+            mask = orc.cautious_mask(W[i], S[i])
+            np.testing.assert_array_equal(host(opt.mask[i]).astype(bool), mask)
+            O = host(opt.update[i])
+            ref = orc.orthogonalize(M[i].astype(np.float64), coeffs)
+            assert orc.rel_fro(O, ref) <= TOL_BF16
+            Wn = orc.store(orc.update_f32(W[i], O, lr, wd, mask), "bf16").astype(np.float32)
+            np.testing.assert_array_equal(host(params[i]), Wn)
+            E[i] = Wn.copy() if t == 1 else orc.ema_f32(E[i], Wn, be)
+            np.testing.assert_array_equal(host(opt.ema[i]), E[i])
+            W[i] = host(params[i])
+        assert opt.step_count == t and opt.ema_count == t
+
+
+def test_blend():
+    announce("blend")
+    shapes = [(64, 96), (96, 64)]
+    _, ws = _make(shapes, "bf16")
+    params = [_dev(w) for w in ws]
+    opt = mo.Muon(params, steps=5, beta_ema=0.9, ema_start=1)
+    for t in range(3):
+        opt.step([_dev(gen.bf16_bits_from_f32(gen.grad_matrix(r, c, 0, t, i, 1e-3)
+                                              .astype(np.float32))) for i, (r, c) in enumerate(shapes)])
+    outs = [torch.empty(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt.blend(outs, 0.35)
+    outs_b = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    opt.blend(outs_b, 0.35)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        want = orc.blend_f32(host(params[i]), host(opt.ema[i]), 0.35)
+        np.testing.assert_array_equal(host(outs[i]), want)
+        np.testing.assert_array_equal(host(outs_b[i]), orc.store(want, "bf16").astype(np.float32))
+
+
+def test_nesterov():
+    announce("nesterov")
+    shapes = [(96, 160)]
+    gs, ws = _make(shapes, "bf16")
+    params = [_dev(w) for w in ws]
+    opt = mo.Muon(params, lr=0.02, beta=0.95, steps=5, nesterov=True, diagnostics=True)
+    opt.step([_dev(g) for g in gs])
+    torch.cuda.synchronize()
+    g = _val(gs[0])
+    M = orc.momentum_f32(np.zeros(shapes[0], np.float32), g, 0.95)
+    U = orc.nesterov_f32(M, g, 0.95)
+    ref = orc.orthogonalize(U.astype(np.float64), _table("quintic", 5))
+    np.testing.assert_array_equal(host(opt.mom[0]), M)
+    assert orc.rel_fro(host(opt.update[0]), ref) <= TOL_BF16
+
+
+def test_zero_gradient_pure_decay():
+    announce("zero gradient")
+    shapes = [(48, 80), (80, 48)]
+    _, ws = _make(shapes, "f32")
+    params = [_dev(w) for w in ws]
+    opt = mo.Muon(params, lr=0.02, wd=1.6, steps=5, diagnostics=True)
+    W = [w.copy() for w in ws]
+    for _ in range(3):
+        opt.step([torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes])
+        W = [orc.update_f32(w, np.zeros_like(w), 0.02, 1.6) for w in W]
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert np.all(host(opt.update[i]) == 0)
+        np.testing.assert_array_equal(host(params[i]), W[i])
+
+
+def test_nan_stays_in_its_matrix():
+    announce("nan confinement")
+    shapes = [(64, 96), (96, 64), (64, 96)]
+    gs, ws = _make(shapes, "bf16")
+    g0 = gen.f32_from_bf16_bits(gs[0]).copy()
+    g0[3, 5] = np.nan
+    gs[0] = gen.bf16_bits_from_f32(g0)
+    params = [_dev(w) for w in ws]
+    opt = mo.Muon(params, steps=5)
+    opt.step([_dev(g) for g in gs])
+    torch.cuda.synchronize()
+    assert np.isnan(host(params[0])).all()
+    assert np.isfinite(host(params[1])).all() and np.isfinite(host(params[2])).all()
+
+
+def test_deterministic_and_resumable():
+    announce("determinism and resume")
+    shapes = [(128, 200), (200, 128), (64, 64)]
+    _, ws = _make(shapes, "bf16")
+
+    def grads(t):
+        return [_dev(gen.bf16_bits_from_f32(gen.grad_matrix(r, c, 5, t, i, 1e-3)
+                                            .astype(np.float32))) for i, (r, c) in enumerate(shapes)]
+
+    def run(n0, n1, resume_from=None):
+        params = [_dev(w) for w in ws]
+        opt = mo.Muon(params, lr=0.02, wd=0.1, beta=0.9, steps=6, beta_slow=0.99,
+                      beta_ema=0.99, cautious=True)
+        if resume_from is not None:
+            sd, pw = resume_from
+            opt.load_state_dict(sd)
+            for p, w in zip(params, pw):
+                p.copy_(w)
+        for t in range(n0, n1):
+            opt.step(grads(t))
+        torch.cuda.synchronize()
+        return opt, params
+
+    a, pa = run(0, 10)
+    b, pb = run(0, 10)
+    for x, y in zip(pa, pb):
+        assert torch.equal(x, y)
+    h, ph = run(0, 5)
+    r, pr = run(5, 10, resume_from=(h.state_dict(), [p.clone() for p in ph]))
+    for x, y in zip(pa, pr):
+        assert torch.equal(x, y)
+    for x, y in zip(a.ema, r.ema):
+        assert torch.equal(x, y)
+    assert r.step_count == 10 and r.ema_count == 10

@@ -195,3 +195,33 @@ def make_inputs(ms: MatrixSet, seed: int = 0, step: int = 0,
         else:
             out.append((g.astype(np.float32), w.astype(np.float32)))
     return out
+
+
+def torch_grad_matrix(rows: int, cols: int, seed: int, step: int, index: int, device,
+                      rms: float | None = 1e-3, dtype=None):
+    """Device-side variant of grad_matrix for large sets: the rank-8 factors
+    come from numpy (same streams as grad_matrix), the iid noise from a torch
+    generator seeded with (seed, step, index).  Returns a device tensor."""
+    import torch
+    rng = np.random.default_rng([seed, step, index])
+    k = min(RANK, rows, cols)
+    p, _ = np.linalg.qr(rng.standard_normal((rows, k)))
+    q, _ = np.linalg.qr(rng.standard_normal((cols, k)))
+    gtr = torch.Generator(device=device)
+    gtr.manual_seed((seed * 1_000_003 + step) * 1_000_003 + index)
+    e = torch.randn((rows, cols), generator=gtr, device=device, dtype=torch.float32)
+    pt = torch.from_numpy((10.0 * p).astype(np.float32)).to(device)
+    qt = torch.from_numpy(q.astype(np.float32)).to(device)
+    g = torch.addmm(e.mul_(0.1), pt, qt.T)
+    if rms is not None:
+        g.mul_(rms / g.square().mean().sqrt())
+    return g if dtype is None else g.to(dtype)
+
+
+def torch_param_matrix(rows: int, cols: int, seed: int, index: int, device, std: float = 0.02,
+                       dtype=None):
+    import torch
+    gtr = torch.Generator(device=device)
+    gtr.manual_seed((seed * 1_000_003 + PARAM_STREAM) * 1_000_003 + index)
+    w = torch.randn((rows, cols), generator=gtr, device=device, dtype=torch.float32).mul_(std)
+    return w if dtype is None else w.to(dtype)
