@@ -58,7 +58,8 @@ double plan_cost(const std::vector<std::pair<std::pair<int, int>, int>>& shapes,
   double gram = 0, poly = 0, apply = 0, gmax = 0, pmax = 0, amax = 0;
   int64_t gt = 0, pt = 0, at = 0;
   for (auto& s : shapes) {
-    const int64_t mp = round_up(s.first.first, ts), np = round_up(s.first.second, ts);
+    const int64_t pad = std::max(ts, 128);
+    const int64_t mp = round_up(s.first.first, pad), np = round_up(s.first.second, pad);
     const int64_t cnt = s.second, tm = mp / ts, tn = np / ts;
     const double tile_g = double(ts) * ts * np, tile_p = double(ts) * ts * mp;
     gt += cnt * tm * (tm + 1) / 2; pt += cnt * tm * (tm + 1) / 2; at += cnt * tm * tn;
@@ -124,9 +125,12 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
   p.off_fprefix = off;
   off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
+  // every padded dimension is a multiple of the tile edge and of two K steps
+  // of the GEMM pipeline (128 elements), so the K loop runs in pairs
+  const int pad = std::max(p.ts, 128);
   for (auto& g : p.groups) {
-    g.mp = int(round_up(g.m, p.ts));
-    g.np = int(round_up(g.n, p.ts));
+    g.mp = int(round_up(g.m, pad));
+    g.np = int(round_up(g.n, pad));
     g.x_elems = int64_t(g.mp) * g.np;
     g.a_elems = int64_t(g.mp) * g.mp;
     g.npart = (g.mp / kEw) * (g.np / kEw);

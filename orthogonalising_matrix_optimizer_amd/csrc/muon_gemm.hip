@@ -5,44 +5,53 @@
 // parameter-update time" of page "きみはNanoGPT speedrunを知っているか？",
 // section "おまけ"; the orthogonalisation itself is described in section
 // "Muonとは").  Three grouped launches per iteration:
-//   GRAM : A = alpha * X X^T            (alpha = s^2 on the first iteration)
-//   POLY : B = b A + c A A              (skipped when c == 0)
+//   GRAM : A = alpha * X X^T             (alpha = s^2 on the first iteration)
+//   POLY : B = b A + c A A               (skipped when c == 0)
 //   APPLY: X' = scale * (a X + beta B X) (scale = s on the first iteration)
 // where s = 1 / (||U||_F + eps) folds the Frobenius normalisation of the
 // first iterate into the products.
 //
 // Tiling: square TS x TS output tiles, 256 threads as a 2 x 2 grid of waves,
-// each wave (TS/2) x (TS/2) built from 32x32 MFMA blocks.  Operands are staged
-// through LDS as "rows with the contraction index contiguous" (128-byte rows,
-// 16-byte chunks XOR-swizzled by row), double-buffered with one barrier per
-// K step.  GRAM and POLY are symmetric: only tiles on or above the diagonal
-// run, and off-diagonal tiles also store their mirror image.  APPLY contracts
-// over the rows of X, so its X operand is transposed in registers on the way
-// into LDS.  The MFMA output layout gives each lane four consecutive rows of
-// one column; the tiles are arranged so that those four values are
-// contiguous in memory (row Q, columns P..P+3 of the stored matrix).
+// each wave (TS/2) x (TS/2) built from 32x32 MFMA blocks.  Every operand tile
+// goes from global memory to LDS by buffer loads with the LDS-DMA bit (no
+// register staging), two LDS stages, one barrier per K step.
+//   * Operands whose contraction index is contiguous in memory (both GRAM
+//     operands, both POLY operands, the B operand of APPLY) are stored as
+//     128-byte rows of 16-byte chunks, the chunk index XOR-swizzled by the row
+//     so that the 32 rows read by one MFMA operand load hit distinct banks.
+//   * APPLY contracts over the rows of X, so its X tile is stored row-major
+//     (contraction index = LDS row) and the bf16 MFMA operand is assembled by
+//     the LDS transpose read (each 16-lane group turns a 4 x 16 block into four
+//     consecutive contraction values per column).
+// GRAM and POLY are symmetric: only tiles on or above the diagonal run, and
+// off-diagonal tiles also store their mirror image.  The MFMA output layout
+// gives each lane four consecutive rows of one column; the tiles are arranged
+// so that those four values are contiguous in memory (row Q, columns P..P+3).
 #include "muon_common.h"
 
 namespace muon {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-// 16-byte chunk as a native vector (plain loads and stores, promotable to registers)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 enum { GRAM = 0, POLY = 1, APPLY = 2 };
+
+// Buffer descriptor word 3 for raw (untyped) loads.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
 template <int XDT> struct Ty;
 template <> struct Ty<kBF16> {
   using T = uint16_t;
-  static constexpr int E = 8;    // elements per 16-byte chunk
+  static constexpr int ES = 2;   // element bytes
   static constexpr int BK = 64;  // contraction elements per K step (128-byte rows)
 };
 template <> struct Ty<kF32> {
   using T = float;
-  static constexpr int E = 4;
+  static constexpr int ES = 4;
   static constexpr int BK = 32;
 };
 
@@ -51,9 +60,6 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return (row << 7) + ((chunk ^ swz(row)) << 4);
 }
 
-__device__ __forceinline__ float bf2f(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
@@ -99,176 +105,201 @@ __device__ __forceinline__ float matrix_scale(const float* partials, int count, 
   return 1.0f / (sqrtf(s) + eps);
 }
 
-// Transpose of an E x E block held as E rows of one 16-byte chunk each:
-// in[q] = row q (E elements), out[c] = column c (E elements).
-__device__ __forceinline__ void transpose_block(const u32x4* in, u32x4* out, uint16_t) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1;
-    uint32_t r[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint32_t lo = in[2 * h][w];
-      const uint32_t hi = in[2 * h + 1][w];
-      r[h] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    out[c] = u32x4{r[0], r[1], r[2], r[3]};
-  }
-}
-__device__ __forceinline__ void transpose_block(const u32x4* in, u32x4* out, float) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t r[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = in[q][c];
-    out[c] = u32x4{r[0], r[1], r[2], r[3]};
-  }
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, uint32_t voff,
+                                      uint32_t soff) {
+#if __HIP_DEVICE_COMPILE__   // the LDS-DMA builtin exists only in the device pass
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+#else
+  (void)rs; (void)lds; (void)voff; (void)soff;
+#endif
 }
 
-template <typename T> struct Chunk { static constexpr int E = 16 / sizeof(T); };
+// Per-block load plan of one operand: buffer descriptor, per-lane offsets
+// (fixed across K steps) and the uniform byte offset of the tile's origin.
+struct OpLoad {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[2];
+  uint32_t origin;     // bytes: first row of the tile (and first column for row-major X)
+  uint32_t ld_bytes;
+};
 
-// Global -> registers for one K step.  K-contiguous operands: thread t takes
-// chunk (t & 7) of rows (t >> 3) + 32u.  The transposed APPLY operand: E x E
-// sub-blocks, E rows of one chunk each.
-template <typename T, int MODE, int TS>
-__device__ __forceinline__ void gemm_gload(const T* pa, const T* pb, int lda, int ldb, int k0,
-                                           int t, u32x4* ra, u32x4* rb) {
-  constexpr int E = Chunk<T>::E;
-  constexpr int NCH = TS / 32;
-  constexpr int NSB = 8 * (TS / E);
-  constexpr int NSBT = (NSB + kThreads - 1) / kThreads;
-  if constexpr (MODE == APPLY) {
+// K-contiguous operand: wave instruction j moves rows 8j..8j+7 (1 KiB); lane L
+// fills physical chunk L & 7 of row 8j + L/8 with the logical chunk that the
+// swizzle maps there.  Rows handled by one wave are j = wave + 4u, whose low
+// three bits alternate between wave and wave + 4.
+__device__ __forceinline__ void plan_kc(OpLoad& o, int lane, int wave) {
 #pragma unroll
-    for (int v = 0; v < NSBT; ++v) {
-      const int sb = t + v * kThreads;
-      if (NSB % kThreads == 0 || sb < NSB) {
-        const int kc = sb / (TS / E), pc = sb - kc * (TS / E);
-        const T* src = pa + static_cast<int64_t>(k0 + kc * E) * lda + pc * E;
-#pragma unroll
-        for (int q = 0; q < E; ++q)
-          ra[v * E + q] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(q) * lda);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int row = (t >> 3) + 32 * u, c = t & 7;
-      ra[u] = *reinterpret_cast<const u32x4*>(pa + static_cast<int64_t>(row) * lda + k0 + c * E);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < NCH; ++u) {
-    const int row = (t >> 3) + 32 * u, c = t & 7;
-    rb[u] = *reinterpret_cast<const u32x4*>(pb + static_cast<int64_t>(row) * ldb + k0 + c * E);
+  for (int x = 0; x < 2; ++x) {
+    const int jl = (wave + 4 * x) & 7;
+    const int c = (lane & 7) ^ (((lane >> 3) ^ jl) & 7);
+    o.voff[x] = static_cast<uint32_t>(lane >> 3) * o.ld_bytes + 16u * c;
   }
 }
 
-// Registers -> LDS stage `buf` (layout [A | B] per stage, 128-byte rows).
-template <typename T, int MODE, int TS>
-__device__ __forceinline__ void gemm_swrite(uint8_t* smem, int buf, int t, const u32x4* ra,
-                                            const u32x4* rb) {
-  constexpr int E = Chunk<T>::E;
-  constexpr int NCH = TS / 32;
-  constexpr int NSB = 8 * (TS / E);
-  constexpr int NSBT = (NSB + kThreads - 1) / kThreads;
-  constexpr int OPB = TS * 128;
-  uint8_t* sa = smem + buf * 2 * OPB;
-  uint8_t* sbp = sa + OPB;
-  if constexpr (MODE == APPLY) {
+template <int TS>
+__device__ __forceinline__ void load_kc(const OpLoad& o, uint32_t kbytes, int wave, uint8_t* dst) {
 #pragma unroll
-    for (int v = 0; v < NSBT; ++v) {
-      const int sb = t + v * kThreads;
-      if (NSB % kThreads == 0 || sb < NSB) {
-        const int kc = sb / (TS / E), pc = sb - kc * (TS / E);
-        u32x4 col[E];
-        transpose_block(ra + v * E, col, T());
-#pragma unroll
-        for (int c = 0; c < E; ++c)
-          *reinterpret_cast<u32x4*>(sa + lds_off(pc * E + c, kc)) = col[c];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int row = (t >> 3) + 32 * u, c = t & 7;
-      *reinterpret_cast<u32x4*>(sa + lds_off(row, c)) = ra[u];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < NCH; ++u) {
-    const int row = (t >> 3) + 32 * u, c = t & 7;
-    *reinterpret_cast<u32x4*>(sbp + lds_off(row, c)) = rb[u];
+  for (int u = 0; u < TS / 32; ++u) {
+    const int j = wave + 4 * u;
+    dma16(o.rs, dst + j * 1024, o.voff[u & 1], o.origin + 8u * j * o.ld_bytes + kbytes);
   }
 }
 
-// MFMA over one LDS stage.  bf16: 32x32x16, lane halves hold contraction
-// elements 0-7 and 8-15 of each 16-step.  fp32: 32x32x2, lane half h feeds
-// elements 8h..8h+7 of each 16-step over eight instructions.
-template <int XDT, int TS>
-__device__ __forceinline__ void gemm_compute(const uint8_t* sa, int lane, int wr, int wc,
-                                             f32x16_t (&acc)[TS / 64][TS / 64]) {
-  constexpr int WT = TS / 2, F = WT / 32, OPB = TS * 128;
-  const uint8_t* sbp = sa + OPB;
+// Row-major X tile of APPLY: BK rows (contraction) of TS elements; instruction
+// j moves RPI = 1024 / (TS * ES) rows; the 16-byte chunk index of row r is
+// XOR-ed with 4 * (r & 1).
+template <int TS, int ES>
+__device__ __forceinline__ void plan_rm(OpLoad& o, int lane) {
+  constexpr int RB = TS * ES, RPI = 1024 / RB, CPR = RB / 16;
+  const int rr = lane / CPR, ch = lane % CPR;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int par = RPI > 1 ? (rr & 1) : p;    // row parity
+    o.voff[p] = static_cast<uint32_t>(rr) * o.ld_bytes + 16u * (ch ^ (4 * par));
+  }
+}
+
+template <int TS, int ES, int BK>
+__device__ __forceinline__ void load_rm(const OpLoad& o, uint32_t k0, int wave, uint8_t* dst) {
+  constexpr int RB = TS * ES, RPI = 1024 / RB, NI = BK / RPI;
+#pragma unroll
+  for (int u = 0; u < NI / 4; ++u) {
+    const int j = wave + 4 * u;
+    dma16(o.rs, dst + j * 1024, o.voff[RPI > 1 ? 0 : (j & 1)],
+          o.origin + (k0 + static_cast<uint32_t>(RPI * j)) * o.ld_bytes);
+  }
+}
+
+// Byte address of element (k, p) in the row-major X tile.
+template <int TS, int ES>
+__device__ __forceinline__ int rm_off(int k, int p) {
+  constexpr int RB = TS * ES, EPC = 16 / ES;
+  return k * RB + (((p / EPC) ^ (4 * (k & 1))) << 4) + (p % EPC) * ES;
+}
+
+// MFMA over one LDS stage.
+template <int XDT, int MODE, int TS>
+__device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* sbp, int lane,
+                                             int wr, int wc, f32x16_t (&acc)[TS / 64][TS / 64]) {
+  constexpr int WT = TS / 2, F = WT / 32;
   const int l32 = lane & 31, hl = lane >> 5;
   if constexpr (XDT == kBF16) {
+    // lane halves hold contraction elements 0-7 and 8-15 of each 16-step.
+    // Fragments of step kk+1 are read while the MFMAs of step kk run.
+    const int g = lane >> 4, i = lane & 15;
+    bf16x8_t fa[2][F], fb[2][F];
+    auto load = [&](int kk, int buf) {
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        if constexpr (MODE == APPLY) {
+          const int kb = 16 * kk + 8 * (g >> 1) + (i >> 2);
+          const int p = wr * WT + f * 32 + 16 * (g & 1) + 4 * (i & 3);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(sa + rm_off<TS, 2>(kb, p)));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(sa + rm_off<TS, 2>(kb + 4, p)));
+          fa[buf][f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          fa[buf][f] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(wr * WT + f * 32 + l32, 2 * kk + hl));
+        }
+        fb[buf][f] = *reinterpret_cast<const bf16x8_t*>(sbp + lds_off(wc * WT + f * 32 + l32, 2 * kk + hl));
+      }
+    };
+    constexpr int NR = (MODE == APPLY ? 3 : 2) * F;   // LDS reads per step
+    constexpr int NM = F * F;                          // MFMAs per step
+    load(0, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 2 * kk + hl;
-      bf16x8_t fa[F], fb[F];
+      const int cur = kk & 1;
+      if (kk < 3) load(kk + 1, cur ^ 1);
 #pragma unroll
-      for (int f = 0; f < F; ++f)
-        fa[f] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(wr * WT + f * 32 + l32, ch));
+      for (int a = 0; a < F; ++a)
 #pragma unroll
-      for (int f = 0; f < F; ++f)
-        fb[f] = *reinterpret_cast<const bf16x8_t*>(sbp + lds_off(wc * WT + f * 32 + l32, ch));
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int b = 0; b < F; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
     }
+#if __HIP_DEVICE_COMPILE__
+    // schedule: first step's reads, then for each step one MFMA per read of
+    // the following step, then the remaining MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int r = 0; r < (NR < NM ? NR : NM); ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+      if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+#endif
   } else {
+    // lane half h feeds contraction elements 8h..8h+7 of each 16-step over
+    // eight 32x32x2 instructions
 #pragma unroll
     for (int g2 = 0; g2 < 2; ++g2) {
       const int ch = 4 * g2 + 2 * hl;
       float fa[F][8], fb[F][8];
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        const int ra_ = wr * WT + f * 32 + l32, rb_ = wc * WT + f * 32 + l32;
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(sa + lds_off(ra_, ch));
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sa + lds_off(ra_, ch + 1));
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sbp + lds_off(rb_, ch));
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sbp + lds_off(rb_, ch + 1));
-        fa[f][0] = a0.x; fa[f][1] = a0.y; fa[f][2] = a0.z; fa[f][3] = a0.w;
-        fa[f][4] = a1.x; fa[f][5] = a1.y; fa[f][6] = a1.z; fa[f][7] = a1.w;
+        const int rb_ = wc * WT + f * 32 + l32;
+        const float4 b0 = *reinterpret_cast<const float4*>(sbp + lds_off(rb_, ch));
+        const float4 b1 = *reinterpret_cast<const float4*>(sbp + lds_off(rb_, ch + 1));
         fb[f][0] = b0.x; fb[f][1] = b0.y; fb[f][2] = b0.z; fb[f][3] = b0.w;
         fb[f][4] = b1.x; fb[f][5] = b1.y; fb[f][6] = b1.z; fb[f][7] = b1.w;
+        if constexpr (MODE == APPLY) {
+          const int p = wr * WT + f * 32 + l32;
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            fa[f][s] = *reinterpret_cast<const float*>(sa + rm_off<TS, 4>(16 * g2 + 8 * hl + s, p));
+        } else {
+          const int ra_ = wr * WT + f * 32 + l32;
+          const float4 a0 = *reinterpret_cast<const float4*>(sa + lds_off(ra_, ch));
+          const float4 a1 = *reinterpret_cast<const float4*>(sa + lds_off(ra_, ch + 1));
+          fa[f][0] = a0.x; fa[f][1] = a0.y; fa[f][2] = a0.z; fa[f][3] = a0.w;
+          fa[f][4] = a1.x; fa[f][5] = a1.y; fa[f][6] = a1.z; fa[f][7] = a1.w;
+        }
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int i = 0; i < F; ++i)
+        for (int a = 0; a < F; ++a)
 #pragma unroll
-          for (int j = 0; j < F; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s], acc[i][j], 0, 0, 0);
+          for (int b = 0; b < F; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
     }
   }
+}
+
+// One K step: start filling `fill` with step kt+1, multiply from `cur`.
+template <int XDT, int MODE, int TS>
+__device__ __forceinline__ void gemm_stage(const OpLoad& la, const OpLoad& lb, int kt, int nk,
+                                           int wave, int lane, int wr, int wc, uint8_t* cur,
+                                           uint8_t* fill, f32x16_t (&acc)[TS / 64][TS / 64]) {
+  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, OPB = TS * 128;
+  if (kt + 1 < nk) {
+    const uint32_t k1 = static_cast<uint32_t>(kt + 1) * BK;
+    if constexpr (MODE == APPLY) load_rm<TS, ES, BK>(la, k1, wave, fill);
+    else load_kc<TS>(la, k1 * ES, wave, fill);
+    load_kc<TS>(lb, k1 * ES, wave, fill + OPB);
+  }
+  gemm_compute<XDT, MODE, TS>(cur, cur + OPB, lane, wr, wc, acc);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 template <int XDT, int MODE, int TS>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
   using T = typename Ty<XDT>::T;
-  constexpr int E = Ty<XDT>::E;
+  constexpr int ES = Ty<XDT>::ES;
   constexpr int BK = Ty<XDT>::BK;
   constexpr int WT = TS / 2;          // wave tile edge
   constexpr int F = WT / 32;          // 32x32 MFMA blocks per wave edge
   constexpr int OPB = TS * 128;       // LDS bytes per operand per stage
-  constexpr int NCH = TS / 32;        // K-contiguous chunks per thread per stage
-  constexpr int NSB = 8 * (TS / E);   // transposed E x E sub-blocks per stage
-  constexpr int NSBT = (NSB + kThreads - 1) / kThreads;
-  constexpr int NA = MODE == APPLY ? NSBT * E : NCH;   // A-operand staging chunks
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[2 * OPB];
   __shared__ float red[4];
 
   // ---- locate group, matrix and tile
@@ -296,32 +327,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
 
   const T* xin = static_cast<const T*>(G.xin) + static_cast<int64_t>(mat) * G.in_stride;
   T* out = static_cast<T*>(G.out) + static_cast<int64_t>(mat) * G.out_stride;
-  const T* pa;
-  const T* pb;
-  int lda, ldb, K;
-  if (MODE == GRAM) {
-    K = G.np; lda = ldb = G.np;
-    pa = xin + static_cast<int64_t>(tP) * TS * G.np;
-    pb = xin + static_cast<int64_t>(tQ) * TS * G.np;
-  } else if (MODE == POLY) {
-    K = G.mp; lda = ldb = G.mp;
-    pa = xin + static_cast<int64_t>(tP) * TS * G.mp;
-    pb = xin + static_cast<int64_t>(tQ) * TS * G.mp;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+
+  OpLoad la, lb;
+  int K;
+  if (MODE == GRAM || MODE == POLY) {
+    const int ld = MODE == GRAM ? G.np : G.mp;
+    K = ld;
+    const uint32_t bytes = static_cast<uint32_t>(G.mp) * ld * ES;
+    la.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xin), 0, bytes, kRsrcWord3);
+    lb.rs = la.rs;
+    la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
+    la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
+    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+    plan_kc(la, lane, wave);
+    plan_kc(lb, lane, wave);
   } else {
-    K = G.mp; lda = G.np; ldb = G.mp;
-    pa = xin + static_cast<int64_t>(tP) * TS;     // rows are k, columns P
-    pb = static_cast<const T*>(G.bop) + static_cast<int64_t>(mat) * G.b_stride +
-         static_cast<int64_t>(tQ) * TS * G.mp;
+    K = G.mp;
+    la.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xin), 0,
+                                              static_cast<uint32_t>(G.mp) * G.np * ES, kRsrcWord3);
+    la.ld_bytes = static_cast<uint32_t>(G.np) * ES;
+    la.origin = static_cast<uint32_t>(tP) * TS * ES;
+    plan_rm<TS, ES>(la, lane);
+    const T* bm = static_cast<const T*>(G.bop) + static_cast<int64_t>(mat) * G.b_stride;
+    lb.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(bm), 0,
+                                              static_cast<uint32_t>(G.mp) * G.mp * ES, kRsrcWord3);
+    lb.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
+    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+    plan_kc(lb, lane, wave);
   }
 
   float scale = 1.f;
   if (args.first) scale = matrix_scale(G.partials + static_cast<int64_t>(mat) * G.p_stride,
                                        G.npartials, args.eps, red);
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-
-  u32x4 ra[NA], rb[NCH];
   f32x16_t acc[F][F];
 #pragma unroll
   for (int i = 0; i < F; ++i)
@@ -331,16 +372,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs args) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = K / BK;
-  gemm_gload<T, MODE, TS>(pa, pb, lda, ldb, 0, t, ra, rb);
-  gemm_swrite<T, MODE, TS>(smem, 0, t, ra, rb);
+  if constexpr (MODE == APPLY) load_rm<TS, ES, BK>(la, 0, wave, smem0);
+  else load_kc<TS>(la, 0, wave, smem0);
+  load_kc<TS>(lb, 0, wave, smem0 + OPB);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // two K steps per trip: the stage being read and the stage being filled are
+  // always different __shared__ objects
+  // (the planner pads every dimension so that nk is even)
 #pragma unroll 1
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gemm_gload<T, MODE, TS>(pa, pb, lda, ldb, (kt + 1) * BK, t, ra, rb);
-    gemm_compute<XDT, TS>(smem + (kt & 1) * 2 * OPB, lane, wr, wc, acc);
-    if (more) gemm_swrite<T, MODE, TS>(smem, (kt + 1) & 1, t, ra, rb);
-    __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    gemm_stage<XDT, MODE, TS>(la, lb, kt, nk, wave, lane, wr, wc, smem0, smem1, acc);
+    gemm_stage<XDT, MODE, TS>(la, lb, kt + 1, nk, wave, lane, wr, wc, smem1, smem0, acc);
   }
 
   // ---- epilogue

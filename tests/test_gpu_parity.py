@@ -153,7 +153,9 @@ def test_step_matches_oracle(dtype, ns):
     torch.cuda.synchronize()
     st = orc.OracleState(shapes)
     w0 = [_val(w).astype(np.float64) for w in ws]
-    ref = orc.muon_step(w0, [_val(g) for g in gs], st, _table("quintic", 5), lr, wd, beta,
+    # the C ABI takes lr and wd as fp32 numbers: the oracle gets the same values
+    lr32, wd32 = float(np.float32(lr)), float(np.float32(wd))
+    ref = orc.muon_step(w0, [_val(g) for g in gs], st, _table("quintic", 5), lr32, wd32, beta,
                         param_dtype=dtype)
     tol = TOL_F32 if ns == "f32" else TOL_BF16
     for i in range(len(shapes)):
@@ -164,13 +166,17 @@ def test_step_matches_oracle(dtype, ns):
         want = orc.store(orc.update_f32(w0[i], O, lr, wd), dtype)
         np.testing.assert_array_equal(host(params[i]).astype(np.float64), want)
         assert np.all(host(opt.mask[i]) == 1)
-        # free-running: within one storage ulp plus lr times the O deviation
+        # free-running: both sides round once to the storage type (at most one
+        # unit in the last place of the larger of the two values; fp32 storage
+        # also carries the fp32 operation rounding, a few units) on top of
+        # lr times the deviation of O
         w = host(params[i]).astype(np.float64)
         wr = ref["params"][i]
-        ulp = np.spacing(np.abs(wr).astype(np.float32)).astype(np.float64) * (
-            2 ** 16 if dtype == "bf16" else 1)
+        big = np.maximum(np.abs(w), np.abs(wr)).astype(np.float32)
+        ulp = np.spacing(big).astype(np.float64) * (2 ** 16 if dtype == "bf16" else 4)
         dev = np.abs(O - ref["O"][i])
-        assert np.all(np.abs(w - wr) <= ulp + lr * dev + 1e-12)
+        excess = np.abs(w - wr) - (ulp + lr32 * dev)
+        assert np.all(excess <= 1e-12), (shapes[i], float(excess.max()))
     assert opt.step_count == 1
 
 
