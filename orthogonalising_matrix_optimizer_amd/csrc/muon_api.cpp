@@ -43,6 +43,7 @@ struct GroupPlan {
 struct Plan {
   int xdt = MUON_BF16;
   int ts = 256;
+  int waves = 4;
   std::vector<GroupPlan> groups;
   std::vector<int> mat_group, mat_slot;
   size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
@@ -116,6 +117,9 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   std::vector<std::pair<std::pair<int, int>, int>> shapes;
   for (auto& g : p.groups) shapes.push_back({{g.m, g.n}, int(g.mats.size())});
   p.ts = choose_ts(shapes);
+  p.waves = 4;
+  if (const char* e = std::getenv("MUON_WAVES"))
+    if (std::atoi(e) == 8 && p.ts == 256) p.waves = 8;
 
   const int es = esize(xdt);
   size_t off = 0;
@@ -159,7 +163,8 @@ const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   std::vector<int64_t> key(2 * size_t(n));
   for (int i = 0; i < n; ++i) { key[2 * i] = rows[i]; key[2 * i + 1] = cols[i]; }
   const char* e = std::getenv("MUON_TILE");
-  const int tile_env = e ? std::atoi(e) : 0;
+  const char* w = std::getenv("MUON_WAVES");
+  const int tile_env = (e ? std::atoi(e) : 0) * 16 + (w ? std::atoi(w) : 0);
   auto k = std::make_tuple(std::move(key), xdt, tile_env);
   auto it = g_plans.find(k);
   if (it != g_plans.end()) return it->second;
@@ -345,7 +350,7 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
         (void)es;
         const int ph = phase == 0 ? MUON_PHASE_GRAM : phase == 1 ? MUON_PHASE_POLY : MUON_PHASE_APPLY;
         probe_begin(ph, s);
-        hipError_t err = launch_gemm(phase, p.xdt, p.ts, ga, blocks, s);
+        hipError_t err = launch_gemm(phase, p.xdt, p.ts, p.waves, ga, blocks, s);
         probe_end(ph, s);
         if (err != hipSuccess) return err;
       }
