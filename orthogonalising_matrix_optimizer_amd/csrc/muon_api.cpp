@@ -44,6 +44,7 @@ struct Plan {
   int xdt = MUON_BF16;
   int ts = 256;
   int waves = 4;
+  int order = 1;   // plain block order: per-XCD tile ranges unbalance mixed-cost groups
   std::vector<GroupPlan> groups;
   std::vector<int> mat_group, mat_slot;
   size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
@@ -120,6 +121,7 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   p.waves = 4;
   if (const char* e = std::getenv("MUON_WAVES"))
     if (std::atoi(e) == 8 && p.ts == 256) p.waves = 8;
+  if (const char* e = std::getenv("MUON_GEMM_ORDER")) p.order = std::atoi(e) & 3;
 
   const int es = esize(xdt);
   size_t off = 0;
@@ -164,7 +166,8 @@ const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   for (int i = 0; i < n; ++i) { key[2 * i] = rows[i]; key[2 * i + 1] = cols[i]; }
   const char* e = std::getenv("MUON_TILE");
   const char* w = std::getenv("MUON_WAVES");
-  const int tile_env = (e ? std::atoi(e) : 0) * 16 + (w ? std::atoi(w) : 0);
+  const char* o = std::getenv("MUON_GEMM_ORDER");
+  const int tile_env = ((e ? std::atoi(e) : 0) * 16 + (w ? std::atoi(w) : 0)) * 4 + (o ? std::atoi(o) & 3 : 0);
   auto k = std::make_tuple(std::move(key), xdt, tile_env);
   auto it = g_plans.find(k);
   if (it != g_plans.end()) return it->second;
@@ -312,6 +315,7 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
     ga.ca = a; ga.cb = b; ga.cc = c;
     ga.cbb = poly ? 1.f : b;
     ga.eps = eps;
+    ga.order = p.order;
     const int es = esize(p.xdt);
     // groups are processed in launch sets of at most kMaxGroups
     for (size_t g0 = 0; g0 < p.groups.size(); g0 += kMaxGroups) {

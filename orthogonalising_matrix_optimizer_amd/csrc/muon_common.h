@@ -88,7 +88,8 @@ struct GemmArgs {
   float ca, cb, cc;       // coefficients of this iteration
   float cbb;              // APPLY: multiplier of the product (1, or b when B = bA)
   float eps;
-  int32_t _pad;
+  int32_t order;          // bit 0: plain block order (no XCD grouping);
+                          // bit 1: row-major APPLY tile order
 };
 
 }  // namespace muon

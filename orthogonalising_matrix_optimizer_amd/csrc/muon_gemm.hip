@@ -11,18 +11,22 @@
 // where s = 1 / (||U||_F + eps) folds the Frobenius normalisation of the
 // first iterate into the products.
 //
-// Tiling: square TS x TS output tiles, 256 threads as a 2 x 2 grid of waves,
-// each wave (TS/2) x (TS/2) built from 32x32 MFMA blocks.  Every operand tile
-// goes from global memory to LDS by buffer loads with the LDS-DMA bit (no
-// register staging), two LDS stages, one barrier per K step.
+// Tiling: square TS x TS output tiles, a WGP x WGQ grid of waves, each wave
+// a sub-tile of 32x32 MFMA blocks.  Every operand tile goes from global memory
+// to LDS by buffer loads with the LDS-DMA bit (no register staging) into a
+// ring of four LDS stages, each holding 64 bytes of contraction per operand
+// row; loads run three stages ahead of the MFMAs, one barrier per stage.
 //   * Operands whose contraction index is contiguous in memory (both GRAM
 //     operands, both POLY operands, the B operand of APPLY) are stored as
-//     128-byte rows of 16-byte chunks, the chunk index XOR-swizzled by the row
-//     so that the 32 rows read by one MFMA operand load hit distinct banks.
+//     64-byte rows of four 16-byte chunks, the chunk index XOR-ed with
+//     (row >> 1) & 3, so the 8 rows read by each 8-lane slice of an MFMA
+//     operand load cover all banks.
 //   * APPLY contracts over the rows of X, so its X tile is stored row-major
-//     (contraction index = LDS row) and the bf16 MFMA operand is assembled by
-//     the LDS transpose read (each 16-lane group turns a 4 x 16 block into four
-//     consecutive contraction values per column).
+//     (contraction index = LDS row, chunk index XOR-ed with 2 (row & 3)) and
+//     the bf16 MFMA operand is assembled by the LDS transpose read (each
+//     16-lane group turns a 4 x 16 block into four consecutive contraction
+//     values per column; its four rows land on four distinct 32-byte bank
+//     slots).
 // GRAM and POLY are symmetric: only tiles on or above the diagonal run, and
 // off-diagonal tiles also store their mirror image.  The MFMA output layout
 // gives each lane four consecutive rows of one column; the tiles are arranged
@@ -42,22 +46,36 @@ enum { GRAM = 0, POLY = 1, APPLY = 2 };
 
 // Buffer descriptor word 3 for raw (untyped) loads.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kStages = 4;
 
 template <int XDT> struct Ty;
 template <> struct Ty<kBF16> {
   using T = uint16_t;
   static constexpr int ES = 2;   // element bytes
-  static constexpr int BK = 64;  // contraction elements per K step (128-byte rows)
+  static constexpr int BK = 32;  // contraction elements per stage (64-byte rows)
 };
 template <> struct Ty<kF32> {
   using T = float;
   static constexpr int ES = 4;
-  static constexpr int BK = 32;
+  static constexpr int BK = 16;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return (row << 7) + ((chunk ^ swz(row)) << 4);
+// LDS bank model: 64 four-byte banks; a 16-byte-per-lane read is served 16
+// lanes (256 bytes) at a time, an 8-byte read 32 lanes at a time.
+//
+// K-contiguous tile: row r, logical 16-byte chunk c (0..3).  Four rows share
+// a 256-byte bank line; XOR-ing the chunk with (r >> 2) & 3 puts the 16 rows
+// read by one 16-lane slice on 16 distinct 16-byte slots.
+__device__ __forceinline__ int kc_off(int r, int c) {
+  return (r << 6) + ((c ^ ((r >> 2) & 3)) << 4);
+}
+// Row-major X tile: contraction row k, column p.  The chunk index is XOR-ed
+// with 4 (k & 3), so the four rows read by two transpose groups (64 bytes
+// each) fall in four different quarters of the bank line.
+template <int TS, int ES>
+__device__ __forceinline__ int rm_off(int k, int p) {
+  constexpr int RB = TS * ES, EPC = 16 / ES, CPR = RB / 16;
+  return k * RB + (((p / EPC) ^ ((4 * (k & 3)) & (CPR - 1))) << 4) + (p % EPC) * ES;
 }
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -91,11 +109,10 @@ __device__ __forceinline__ void st4(float* p, const float* v) {
 __device__ __forceinline__ void st1(uint16_t* p, float v) { *p = f2bf(v); }
 __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
 
-// 1 / (sqrt(sum of the matrix's norm partials) + eps), same summation order in
-// every block of the matrix.
-// Summation order: 256-strided per-thread sums over the first four waves'
-// lanes, then the butterfly, then the wave totals in order -- the same in
-// every kernel and block size, so every block of a matrix gets the same s.
+// 1 / (sqrt(sum of the matrix's norm partials) + eps).  Summation order:
+// 256-strided per-thread sums over the first four waves' lanes, the
+// butterfly, then the wave totals in order -- the same in every kernel and
+// block size, so every block of a matrix gets the same s.
 template <int NW>
 __device__ __forceinline__ float matrix_scale(const float* partials, int count, float eps,
                                               float* red) {
@@ -110,77 +127,107 @@ __device__ __forceinline__ float matrix_scale(const float* partials, int count, 
   return 1.0f / (sqrtf(s) + eps);
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, uint32_t voff,
-                                      uint32_t soff) {
-#if __HIP_DEVICE_COMPILE__   // the LDS-DMA builtin exists only in the device pass
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
-#else
-  (void)rs; (void)lds; (void)voff; (void)soff;
-#endif
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes at `base` (reads past the end
+// return zero).  All fields are block-uniform and live in SGPRs.
+__device__ __forceinline__ u32x4_t make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t d;
+  d[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  d[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = kRsrcWord3;
+  return d;
 }
 
-// Per-block load plan of one operand: buffer descriptor, per-lane offsets
-// (fixed across K steps) and the uniform byte offset of the tile's origin.
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+
+// One 1 KiB LDS-DMA load: lane L copies 16 bytes from global offset
+// voff + soff of the descriptor's buffer to LDS address lds + 16 L.  It is
+// issued as inline assembly so that the compiler does not order later LDS
+// reads of *other* stage buffers behind it; wait_vm orders it explicitly.
+// It has no result register.
+// (M0 is reserved for the compiler's own M0 users, which set it right before
+// each use; the clobber keeps it from assuming a value survives.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const u32x4_t& d, uint32_t lds, uint32_t voff,
+                                      uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(d), "s"(soff)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most n of this wave's vector loads are outstanding (loads
+// complete in issue order); LDS and export counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence.  Stage data arrive by LDS DMA
+// and are covered by wait_vm before it; fragments of the previous stage are
+// already in registers (consumed by its MFMAs) when a wave reaches it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Per-block load plan of one operand: buffer descriptor, per-lane offset
+// (fixed across stages) and the uniform byte offset of the tile's origin.
 struct OpLoad {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t voff[2];
+  u32x4_t rs;
+  uint32_t voff;
   uint32_t origin;     // bytes: first row of the tile (and first column for row-major X)
   uint32_t ld_bytes;
 };
 
-// K-contiguous operand: wave instruction j moves rows 8j..8j+7 (1 KiB); lane L
-// fills physical chunk L & 7 of row 8j + L/8 with the logical chunk that the
-// swizzle maps there.  Rows handled by one of NW waves are j = wave + NW u,
-// whose low three bits take at most two values (wave, wave + NW).
-template <int NW>
-__device__ __forceinline__ void plan_kc(OpLoad& o, int lane, int wave) {
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int jl = (wave + NW * x) & 7;
-    const int c = (lane & 7) ^ (((lane >> 3) ^ jl) & 7);
-    o.voff[x] = static_cast<uint32_t>(lane >> 3) * o.ld_bytes + 16u * c;
-  }
+// K-contiguous operand: instruction j moves rows 16j..16j+15 (1 KiB); lane L
+// fills physical chunk L & 3 of row 16j + L/4 with the logical chunk the
+// swizzle maps there, (L & 3) ^ ((L >> 4) & 3) for every j.
+__device__ __forceinline__ void plan_kc(OpLoad& o, int lane) {
+  o.voff = static_cast<uint32_t>(lane >> 2) * o.ld_bytes + 16u * ((lane & 3) ^ ((lane >> 4) & 3));
 }
 
 template <int TS, int NW>
 __device__ __forceinline__ void load_kc(const OpLoad& o, uint32_t kbytes, int wave, uint8_t* dst) {
 #pragma unroll
-  for (int u = 0; u < TS / (8 * NW); ++u) {
+  for (int u = 0; u < TS / (16 * NW); ++u) {
     const int j = wave + NW * u;
-    dma16(o.rs, dst + j * 1024, o.voff[NW < 8 ? (u & 1) : 0], o.origin + 8u * j * o.ld_bytes + kbytes);
+    dma16(o.rs, lds_addr(dst) + j * 1024, o.voff, o.origin + 16u * j * o.ld_bytes + kbytes);
   }
 }
 
-// Row-major X tile of APPLY: BK rows (contraction) of TS elements; instruction
-// j moves RPI = 1024 / (TS * ES) rows; the 16-byte chunk index of row r is
-// XOR-ed with 4 * (r & 1).
-template <int TS, int ES>
-__device__ __forceinline__ void plan_rm(OpLoad& o, int lane) {
+// Row-major X tile of APPLY: BK rows of TS elements; instruction j moves
+// RPI = 1024 / (TS ES) rows.  With NW a multiple of four every instruction
+// of a wave has j = wave (mod 4), so the row's low two bits -- and the lane's
+// offset -- are fixed per lane.
+template <int TS, int ES, int NW>
+__device__ __forceinline__ void plan_rm(OpLoad& o, int lane, int wave) {
+  static_assert(NW % 4 == 0, "wave count");
   constexpr int RB = TS * ES, RPI = 1024 / RB, CPR = RB / 16;
   const int rr = lane / CPR, ch = lane % CPR;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int par = RPI > 1 ? (rr & 1) : p;    // row parity
-    o.voff[p] = static_cast<uint32_t>(rr) * o.ld_bytes + 16u * (ch ^ (4 * par));
-  }
+  const int r3 = (RPI * wave + rr) & 3;
+  o.voff = static_cast<uint32_t>(rr) * o.ld_bytes + 16u * (ch ^ ((4 * r3) & (CPR - 1)));
 }
 
 template <int TS, int ES, int BK, int NW>
 __device__ __forceinline__ void load_rm(const OpLoad& o, uint32_t k0, int wave, uint8_t* dst) {
   constexpr int RB = TS * ES, RPI = 1024 / RB, NI = BK / RPI;
+  static_assert(NI % NW == 0, "row-major load split");
 #pragma unroll
   for (int u = 0; u < NI / NW; ++u) {
     const int j = wave + NW * u;
-    dma16(o.rs, dst + j * 1024, o.voff[RPI > 1 ? 0 : (j & 1)],
+    dma16(o.rs, lds_addr(dst) + j * 1024, o.voff,
           o.origin + (k0 + static_cast<uint32_t>(RPI * j)) * o.ld_bytes);
   }
-}
-
-// Byte address of element (k, p) in the row-major X tile.
-template <int TS, int ES>
-__device__ __forceinline__ int rm_off(int k, int p) {
-  constexpr int RB = TS * ES, EPC = 16 / ES;
-  return k * RB + (((p / EPC) ^ (4 * (k & 1))) << 4) + (p % EPC) * ES;
 }
 
 // MFMA over one LDS stage; the wave at (wr, wc) of a WGP x WGQ grid owns a
@@ -192,11 +239,13 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
   constexpr int WTP = TS / WGP, WTQ = TS / WGQ, FP = WTP / 32, FQ = WTQ / 32;
   const int l32 = lane & 31, hl = lane >> 5;
   if constexpr (XDT == kBF16) {
-    // lane halves hold contraction elements 0-7 and 8-15 of each 16-step.
-    // Fragments of step kk+1 are read while the MFMAs of step kk run.
+    // lane halves hold contraction elements 0-7 and 8-15 of each 16-step;
+    // the fragments of the second step are read while the first step's
+    // MFMAs run
     const int g = lane >> 4, i = lane & 15;
     bf16x8_t fa[2][FP], fb[2][FQ];
-    auto load = [&](int kk, int buf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int f = 0; f < FP; ++f) {
         if constexpr (MODE == APPLY) {
@@ -206,101 +255,104 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
               (lds_i16x4_t*)(sa + rm_off<TS, 2>(kb, p)));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_i16x4_t*)(sa + rm_off<TS, 2>(kb + 4, p)));
-          fa[buf][f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          fa[kk][f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-          fa[buf][f] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(wr * WTP + f * 32 + l32, 2 * kk + hl));
+          fa[kk][f] = *reinterpret_cast<const bf16x8_t*>(sa + kc_off(wr * WTP + f * 32 + l32, 2 * kk + hl));
         }
       }
 #pragma unroll
       for (int f = 0; f < FQ; ++f)
-        fb[buf][f] = *reinterpret_cast<const bf16x8_t*>(sbp + lds_off(wc * WTQ + f * 32 + l32, 2 * kk + hl));
-    };
-    constexpr int NR = (MODE == APPLY ? 2 : 1) * FP + FQ;   // LDS reads per step
-    constexpr int NM = FP * FQ;                             // MFMAs per step
-    load(0, 0);
+        fb[kk][f] = *reinterpret_cast<const bf16x8_t*>(sbp + kc_off(wc * WTQ + f * 32 + l32, 2 * kk + hl));
+    }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1;
-      if (kk < 3) load(kk + 1, cur ^ 1);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int a = 0; a < FP; ++a)
 #pragma unroll
         for (int b = 0; b < FQ; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
-    }
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][a], fb[kk][b], acc[a][b], 0, 0, 0);
 #if __HIP_DEVICE_COMPILE__
-    // schedule: first step's reads, then for each step one MFMA per read of
-    // the following step, then the remaining MFMAs
+    constexpr int NR = (MODE == APPLY ? 2 : 1) * FP + FQ;   // LDS reads per 16-step
+    constexpr int NM = FP * FQ;                             // MFMAs per 16-step
+    constexpr int NI = NR < NM ? NR : NM;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-#pragma unroll
-      for (int r = 0; r < (NR < NM ? NR : NM); ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
-      if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+    for (int r = 0; r < NI; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
 #endif
   } else {
-    // lane half h feeds contraction elements 8h..8h+7 of each 16-step over
-    // eight 32x32x2 instructions
+    // lane half h feeds contraction elements 8h..8h+7 over eight 32x32x2
+    // instructions
+    float fa[FP][8], fb[FQ][8];
 #pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      const int ch = 4 * g2 + 2 * hl;
-      float fa[FP][8], fb[FQ][8];
-#pragma unroll
-      for (int f = 0; f < FQ; ++f) {
-        const int rb_ = wc * WTQ + f * 32 + l32;
-        const float4 b0 = *reinterpret_cast<const float4*>(sbp + lds_off(rb_, ch));
-        const float4 b1 = *reinterpret_cast<const float4*>(sbp + lds_off(rb_, ch + 1));
-        fb[f][0] = b0.x; fb[f][1] = b0.y; fb[f][2] = b0.z; fb[f][3] = b0.w;
-        fb[f][4] = b1.x; fb[f][5] = b1.y; fb[f][6] = b1.z; fb[f][7] = b1.w;
-      }
-#pragma unroll
-      for (int f = 0; f < FP; ++f) {
-        if constexpr (MODE == APPLY) {
-          const int p = wr * WTP + f * 32 + l32;
-#pragma unroll
-          for (int s = 0; s < 8; ++s)
-            fa[f][s] = *reinterpret_cast<const float*>(sa + rm_off<TS, 4>(16 * g2 + 8 * hl + s, p));
-        } else {
-          const int ra_ = wr * WTP + f * 32 + l32;
-          const float4 a0 = *reinterpret_cast<const float4*>(sa + lds_off(ra_, ch));
-          const float4 a1 = *reinterpret_cast<const float4*>(sa + lds_off(ra_, ch + 1));
-          fa[f][0] = a0.x; fa[f][1] = a0.y; fa[f][2] = a0.z; fa[f][3] = a0.w;
-          fa[f][4] = a1.x; fa[f][5] = a1.y; fa[f][6] = a1.z; fa[f][7] = a1.w;
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int a = 0; a < FP; ++a)
-#pragma unroll
-          for (int b = 0; b < FQ; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
+    for (int f = 0; f < FQ; ++f) {
+      const int rb_ = wc * WTQ + f * 32 + l32;
+      const float4 b0 = *reinterpret_cast<const float4*>(sbp + kc_off(rb_, 2 * hl));
+      const float4 b1 = *reinterpret_cast<const float4*>(sbp + kc_off(rb_, 2 * hl + 1));
+      fb[f][0] = b0.x; fb[f][1] = b0.y; fb[f][2] = b0.z; fb[f][3] = b0.w;
+      fb[f][4] = b1.x; fb[f][5] = b1.y; fb[f][6] = b1.z; fb[f][7] = b1.w;
     }
+#pragma unroll
+    for (int f = 0; f < FP; ++f) {
+      if constexpr (MODE == APPLY) {
+        const int p = wr * WTP + f * 32 + l32;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          fa[f][s] = *reinterpret_cast<const float*>(sa + rm_off<TS, 4>(8 * hl + s, p));
+      } else {
+        const int ra_ = wr * WTP + f * 32 + l32;
+        const float4 a0 = *reinterpret_cast<const float4*>(sa + kc_off(ra_, 2 * hl));
+        const float4 a1 = *reinterpret_cast<const float4*>(sa + kc_off(ra_, 2 * hl + 1));
+        fa[f][0] = a0.x; fa[f][1] = a0.y; fa[f][2] = a0.z; fa[f][3] = a0.w;
+        fa[f][4] = a1.x; fa[f][5] = a1.y; fa[f][6] = a1.z; fa[f][7] = a1.w;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int a = 0; a < FP; ++a)
+#pragma unroll
+        for (int b = 0; b < FQ; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a][s], fb[b][s], acc[a][b], 0, 0, 0);
   }
 }
 
-// One K step: start filling `fill` with step kt+1, multiply from `cur`.
+// Issue the loads of stage k into buffer `dst` ([A | B]).
+template <int XDT, int MODE, int TS, int NW>
+__device__ __forceinline__ void gemm_issue(const OpLoad& la, const OpLoad& lb, int k, int wave,
+                                           uint8_t* dst) {
+  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, OPB = TS * 64;
+  const uint32_t k0 = static_cast<uint32_t>(k) * BK;
+  if constexpr (MODE == APPLY) load_rm<TS, ES, BK, NW>(la, k0, wave, dst);
+  else load_kc<TS, NW>(la, k0 * ES, wave, dst);
+  load_kc<TS, NW>(lb, k0 * ES, wave, dst + OPB);
+}
+
+// One stage: wait for stage k, refill the buffer of stage k-1 with stage k+3,
+// multiply from stage k.
 template <int XDT, int MODE, int TS, int WGP, int WGQ>
-__device__ __forceinline__ void gemm_stage(const OpLoad& la, const OpLoad& lb, int kt, int nk,
-                                           int wave, int lane, int wr, int wc, uint8_t* cur,
-                                           uint8_t* fill,
-                                           f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
-  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, OPB = TS * 128, NW = WGP * WGQ;
-  if (kt + 1 < nk) {
-    const uint32_t k1 = static_cast<uint32_t>(kt + 1) * BK;
-    if constexpr (MODE == APPLY) load_rm<TS, ES, BK, NW>(la, k1, wave, fill);
-    else load_kc<TS, NW>(la, k1 * ES, wave, fill);
-    load_kc<TS, NW>(lb, k1 * ES, wave, fill + OPB);
-  }
+__device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, int k, int nk,
+                                          int wave, int lane, int wr, int wc, uint8_t* cur,
+                                          uint8_t* fill,
+                                          f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
+  constexpr int NW = WGP * WGQ, OPB = TS * 64;
+  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK;
+  constexpr int NA = MODE == APPLY ? BK / (1024 / (TS * ES)) / NW : TS / (16 * NW);
+  constexpr int PER = NA + TS / (16 * NW);   // loads per wave per stage
+  const int ahead = nk - 1 - k;              // stages issued after this one: min(2, ahead)
+  if (ahead >= 2) wait_vm<2 * PER>();
+  else if (ahead == 1) wait_vm<PER>();
+  else wait_vm<0>();
+  // bare barrier: a fenced __syncthreads would also wait for the loads of the
+  // stages still in flight
+  lds_barrier();
+  if (k + 3 < nk) gemm_issue<XDT, MODE, TS, NW>(la, lb, k + 3, wave, fill);
   gemm_compute<XDT, MODE, TS, WGP, WGQ>(cur, cur + OPB, lane, wr, wc, acc);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 }
 
 // Logical block index: blocks are dealt round-robin to the eight XCDs; this
@@ -320,14 +372,16 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   constexpr int NW = WGP * WGQ;       // waves per block
   constexpr int WTP = TS / WGP, WTQ = TS / WGQ;
   constexpr int FP = WTP / 32, FQ = WTQ / 32;
-  constexpr int OPB = TS * 128;       // LDS bytes per operand per stage
+  constexpr int OPB = TS * 64;        // LDS bytes per operand per stage
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[2 * OPB];
   __shared__ float red[NW];
 
   // ---- locate group, matrix and tile
-  const int bid = xcd_block();
+  const int bid = (args.order & 1) ? static_cast<int>(blockIdx.x) : xcd_block();
   // constant-index selection keeps the group table in kernel-argument space
   GemmGroup G = args.g[0];
 #pragma unroll
@@ -337,7 +391,10 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   const int mat = local / G.tiles;
   const int tile = local - mat * G.tiles;
   int tP, tQ;
-  if (MODE == APPLY) {
+  if (MODE == APPLY && (args.order & 2)) {
+    tP = tile % (G.np / TS);
+    tQ = tile / (G.np / TS);
+  } else if (MODE == APPLY) {
     // groups of up to four row panels (Q), column panels (P) outer
     const int tn = G.np / TS, tm = G.mp / TS;
     const int grp = tile / (4 * tn), q0 = 4 * grp;
@@ -365,26 +422,24 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
     const int ld = MODE == GRAM ? G.np : G.mp;
     K = ld;
     const uint32_t bytes = static_cast<uint32_t>(G.mp) * ld * ES;
-    la.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xin), 0, bytes, kRsrcWord3);
+    la.rs = make_desc(xin, bytes);
     lb.rs = la.rs;
     la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
     la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
     lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
-    plan_kc<NW>(la, lane, wave);
-    plan_kc<NW>(lb, lane, wave);
+    plan_kc(la, lane);
+    plan_kc(lb, lane);
   } else {
     K = G.mp;
-    la.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xin), 0,
-                                              static_cast<uint32_t>(G.mp) * G.np * ES, kRsrcWord3);
+    la.rs = make_desc(xin, static_cast<uint32_t>(G.mp) * G.np * ES);
     la.ld_bytes = static_cast<uint32_t>(G.np) * ES;
     la.origin = static_cast<uint32_t>(tP) * TS * ES;
-    plan_rm<TS, ES>(la, lane);
+    plan_rm<TS, ES, NW>(la, lane, wave);
     const T* bm = static_cast<const T*>(G.bop) + static_cast<int64_t>(mat) * G.b_stride;
-    lb.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(bm), 0,
-                                              static_cast<uint32_t>(G.mp) * G.mp * ES, kRsrcWord3);
+    lb.rs = make_desc(bm, static_cast<uint32_t>(G.mp) * G.mp * ES);
     lb.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
     lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
-    plan_kc<NW>(lb, lane, wave);
+    plan_kc(lb, lane);
   }
 
   float scale = 1.f;
@@ -399,44 +454,32 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // the planner pads every dimension to a multiple of 128, so nk is a
+  // multiple of four and each trip below runs the four ring buffers in order
   const int nk = K / BK;
-  if constexpr (MODE == APPLY) load_rm<TS, ES, BK, NW>(la, 0, wave, smem0);
-  else load_kc<TS, NW>(la, 0, wave, smem0);
-  load_kc<TS, NW>(lb, 0, wave, smem0 + OPB);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // two K steps per trip: the stage being read and the stage being filled are
-  // always different __shared__ objects
-  // (the planner pads every dimension so that nk is even)
+  gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
+  gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1);
+  gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2);
 #pragma unroll 1
-  for (int kt = 0; kt < nk; kt += 2) {
-    gemm_stage<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, smem0, smem1, acc);
-    gemm_stage<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, smem1, smem0, acc);
+  for (int kt = 0; kt < nk; kt += kStages) {
+    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, acc);
+    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, acc);
+    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, acc);
   }
 
   // ---- epilogue
   const int ld_out = MODE == APPLY ? G.np : G.mp;
   const float alpha = MODE == GRAM ? scale * scale : 1.f;
-  // off-diagonal symmetric tiles also store the transposed tile; bf16 tiles
-  // stage it in the (now idle) LDS so that it leaves as 16-byte rows
   const bool mirror = MODE != APPLY && tP != tQ;
-  constexpr bool kStage = XDT == kBF16 && MODE != APPLY;
-  constexpr int SP = TS * 2;                 // staged row pitch (bytes)
-  // staged row r (= P - tP*TS) lives in smem0 for r < TS/2, else in smem1
-  static_assert(!kStage || (TS / 2) * SP <= 2 * OPB, "mirror staging does not fit");
-  auto srow = [&](int r) -> uint8_t* {
-    return (r < TS / 2 ? smem0 : smem1) + (r % (TS / 2)) * SP;
-  };
 #pragma unroll
   for (int i = 0; i < FP; ++i) {
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
-      const int ql = wc * WTQ + j * 32 + (lane & 31);
-      const int Q = tQ * TS + ql;
+      const int Q = tQ * TS + wc * WTQ + j * 32 + (lane & 31);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int pl = wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
-        const int P = tP * TS + pl;
+        const int P = tP * TS + wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][rg * 4 + e];
@@ -457,32 +500,9 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
         }
         st4(out + qp, v);
         if (mirror) {
-          if constexpr (kStage) {
-            // row pl+e, column ql; 16-byte chunks XOR 4 on every fourth row
-            // group so the two lane halves land on different banks
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = pl + e;
-              const int off = ((((ql >> 3) ^ (4 * ((r >> 2) & 1)))) << 4) + (ql & 7) * 2;
-              *reinterpret_cast<uint16_t*>(srow(r) + off) = f2bf(v[e]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) st1(out + static_cast<int64_t>(P + e) * ld_out + Q, v[e]);
-          }
+          for (int e = 0; e < 4; ++e) st1(out + static_cast<int64_t>(P + e) * ld_out + Q, v[e]);
         }
-      }
-    }
-  }
-  if constexpr (kStage) {
-    if (mirror) {
-      __syncthreads();
-      constexpr int CPRW = TS / 8;           // 16-byte chunks per staged row
-      for (int c = t; c < TS * CPRW; c += 64 * NW) {
-        const int r = c / CPRW, ch = c % CPRW;
-        const int pch = ch ^ (4 * ((r >> 2) & 1));
-        const uint4 vv = *reinterpret_cast<const uint4*>(srow(r) + (pch << 4));
-        *reinterpret_cast<uint4*>(out + static_cast<int64_t>(tP * TS + r) * ld_out + tQ * TS + ch * 8) = vv;
       }
     }
   }
