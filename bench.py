@@ -1,0 +1,219 @@
+"""Benchmark of the Muon-style optimizer step on one MI355X.
+
+One "step" is one call of muon_step over the whole 124M GPT-2-shaped matrix
+set (72 bf16 matrices: 12 layers x {Q, K, V, O 768x768; MLP 768x3072;
+MLP 3072x768}), fp32 momentum, five quintic Newton-Schulz iterations, grouped
+by effective shape: momentum, norm, 5 x (Gram, polynomial, apply), update.
+Inputs are synthetic (seeded low-rank + noise gradients at entry RMS 1e-3,
+0.02 N(0,1) parameters) and resident in HBM before the timed region.
+
+Prints one JSON line.  Extra fields: NS TFLOP/s (symmetric flop count),
+per-kernel times, the roofline of the dominant kernel (the APPLY GEMM,
+timed live with HIP events around its launches in the timed region) and the
+CPU oracle timed on the host on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_apply_gpt124m.json")
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("muon_gemm.hip", "muon_common.h"):
+        with open(os.path.join(ROOT, "orthogonalising_matrix_optimizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(launch_flops_key: str):
+    """HBM bytes per APPLY launch from the committed counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha256_16") != _src_hash() or t.get("workload") != launch_flops_key:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def apply_flops(shapes) -> float:
+    """Algorithmic flops of one APPLY launch: 2 m^2 n per matrix."""
+    tot = 0.0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        tot += 2.0 * m * m * n
+    return tot
+
+
+def elementwise_bytes(shapes):
+    """Algorithmic HBM bytes of the prepare and finish kernels (plain Muon,
+    bf16 params/grads/iterate, fp32 momentum): prepare reads G (2) and M (4),
+    writes M (4) and X0 (2); finish reads O (2) and W (2), writes W (2)."""
+    n = sum(r * c for r, c in shapes)
+    return 12.0 * n, 6.0 * n
+
+
+def cpu_baseline(shapes, grads_bits, params_bits, coeffs, lr, wd, beta):
+    """The CPU oracle (fp64 numpy) on one full optimizer step of the same set."""
+    import threadpoolctl
+    from oracle import muon_oracle as orc
+    from workloads import gen
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    grads = [gen.f32_from_bf16_bits(g) for g in grads_bits]
+    params = [gen.f32_from_bf16_bits(w).astype(np.float64) for w in params_bits]
+    st = orc.OracleState(shapes)
+    t0 = time.perf_counter()
+    orc.muon_step(params, grads, st, coeffs, lr, wd, beta, param_dtype="bf16", keep=False)
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 5), "unit": "optimizer steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one full step of the same {len(shapes)}-matrix set on the host "
+                      f"({dt:.2f} s, fp64 numpy/OpenBLAS)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("this benchmark runs on one GPU only: the optimizer step is measured on a single "
+              "MI355X (the multi-GPU layout is a design note, not a measured path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import orthogonalising_matrix_optimizer_amd as mo
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
+        return
+
+    ms = gen.SETS["gpt124m"]
+    shapes = list(ms.shapes)
+    coeffs = gen.coeff_table(ms.coeffs, ms.steps)
+    inputs = gen.make_inputs(ms, seed=0)
+    grads_bits = [g for g, _ in inputs]
+    params_bits = [w for _, w in inputs]
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    params = [to_dev(w) for w in params_bits]
+    grads = [to_dev(g) for g in grads_bits]
+    opt = mo.Muon(params, lr=ms.lr, wd=ms.wd, beta=ms.beta, steps=ms.steps, coeffs=coeffs,
+                  ns_dtype="bf16")
+    plan = mo.plan_info(shapes, ms.steps, coeffs)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        opt.step(grads)
+    torch.cuda.synchronize()
+
+    # timed region; the APPLY launches are bracketed with HIP events on the
+    # launch stream
+    n_apply = args.steps * ms.steps
+    mo.probe_arm("apply", n_apply)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        opt.step(grads)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    apply_ms = mo.probe_read(n_apply)
+    mo.probe_disarm()
+
+    # per-phase averages from a short extra run (not part of the timed region)
+    phase_ms = {}
+    for ph in ("prepare", "gram", "poly", "finish"):
+        cap = 5 * (ms.steps if ph in ("gram", "poly") else 1)
+        mo.probe_arm(ph, cap)
+        for _ in range(5):
+            opt.step(grads)
+        torch.cuda.synchronize()
+        t = mo.probe_read(cap)
+        mo.probe_disarm()
+        phase_ms[ph] = round(float(np.mean(t)), 4) if t else None
+    phase_ms["apply"] = round(float(np.mean(apply_ms)), 4) if apply_ms else None
+
+    sym, dense = gen.ns_flops(shapes, ms.steps)
+    a_flops = apply_flops(shapes)
+    a_tf = a_flops / (phase_ms["apply"] * 1e-3) / 1e12
+    key = f"gpt124m:{ms.steps}:{ms.coeffs}"
+    traffic = _traffic(key)
+    prep_b, fin_b = elementwise_bytes(shapes)
+    steps_per_s = 1000.0 / ms_step
+    out = {
+        "metric": "optimizer steps/sec + NS TFLOP/s (% MFMA peak), 124M-GPT matrix set, 1 GPU",
+        "value": round(steps_per_s, 3),
+        "unit": "optimizer steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded low-rank+noise gradients, random-init bf16 parameters)",
+        "config": {"workload": "gpt124m matrix set: 72 bf16 matrices (48x 768x768, "
+                               "12x 768x3072, 12x 3072x768), fp32 momentum, Muon step, "
+                               "5 quintic Newton-Schulz iterations, grouped by shape",
+                   "matrices": len(shapes), "elements": int(sum(r * c for r, c in shapes)),
+                   "ns_steps": ms.steps, "coeffs": "quintic (15/8, -10/8, 3/8)",
+                   "groups": plan["groups"], "tile": plan["tile"],
+                   "launches_per_step": plan["launches_per_step"]},
+        "ns_tflops": round(sym / (ms_step * 1e-3) / 1e12, 2),
+        "ns_frac_mfma_peak": round(sym / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ns_flops_per_step": {"symmetric": sym, "dense_equivalent": dense},
+        "kernel_ms": phase_ms,
+        "elementwise_gbs": {
+            "prepare": round(prep_b / (phase_ms["prepare"] * 1e-3) / 1e9, 1),
+            "finish": round(fin_b / (phase_ms["finish"] * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "kernel": "APPLY (X <- aX + BX, bf16 MFMA)",
+                     "achieved": round(a_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": a_flops, "launches_timed": len(apply_ms)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shapes, grads_bits, params_bits, coeffs, ms.lr,
+                                           ms.wd, ms.beta)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -118,9 +118,11 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   std::vector<std::pair<std::pair<int, int>, int>> shapes;
   for (auto& g : p.groups) shapes.push_back({{g.m, g.n}, int(g.mats.size())});
   p.ts = choose_ts(shapes);
-  p.waves = 4;
+  // 256-wide bf16 tiles run eight waves (two per SIMD); MUON_WAVES=4 selects
+  // the one-wave-per-SIMD variant
+  p.waves = (p.ts == 256 && xdt == MUON_BF16) ? 8 : 4;
   if (const char* e = std::getenv("MUON_WAVES"))
-    if (std::atoi(e) == 8 && p.ts == 256) p.waves = 8;
+    if (std::atoi(e) == 4) p.waves = 4;
   if (const char* e = std::getenv("MUON_GEMM_ORDER")) p.order = std::atoi(e) & 3;
 
   const int es = esize(xdt);
