@@ -77,6 +77,24 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (returned as float32), ties to even.
+
+    Same result as round_to_bf16 for float32 inputs (checked by the pins);
+    works on the bit pattern: keep the top 16 bits, adding half of the
+    dropped part rounded to even.
+    """
+    x = np.ascontiguousarray(x, dtype=F32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)).view(F32)
+    nan = np.isnan(x)
+    if nan.any():
+        r = r.copy()
+        r[nan] = np.nan
+    return r
+
+
 # ----------------------------------------------------------------------------
 # Newton-Schulz style orthogonalisation (float64)
 def ns_poly_scalar(x: float, coeffs: np.ndarray) -> float:
@@ -163,8 +181,10 @@ def blend_f32(W: np.ndarray, E: np.ndarray, w_final: float) -> np.ndarray:
 
 
 def store(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round a float64 result to the storage type ("bf16", "f32" or "f64")."""
+    """Round a result to the storage type ("bf16", "f32" or "f64")."""
     if dtype == "bf16":
+        if np.asarray(x).dtype == F32:
+            return round_f32_to_bf16(x).astype(np.float64)
         return round_to_bf16(x)
     if dtype == "f64":
         return np.asarray(x, dtype=np.float64)

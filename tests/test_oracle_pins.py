@@ -57,6 +57,14 @@ def test_bf16_known_values():
     assert np.isnan(orc.round_to_bf16(np.array([np.nan]))[0])
 
 
+def test_bf16_fast_path_matches_definition():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(300000) * np.exp(rng.uniform(-40, 40, 300000))).astype(np.float32)
+    x[:4] = [np.float32(1 + 2 ** -8), np.float32(1 + 3 * 2 ** -8), np.float32(-0.0), np.float32(3.4e38)]
+    np.testing.assert_array_equal(orc.round_f32_to_bf16(x).astype(np.float64),
+                                  orc.round_to_bf16(x.astype(np.float64)))
+
+
 def test_bf16_matches_bit_rounding_on_fp32_inputs():
     # An independent implementation (integer rounding of fp32 bit patterns)
     rng = np.random.default_rng(1)
