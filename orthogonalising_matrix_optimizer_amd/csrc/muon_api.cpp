@@ -13,7 +13,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <cstdio>
 #include <mutex>
+#include <string>
 #include <tuple>
 #include <vector>
 
@@ -44,7 +46,10 @@ struct Plan {
   int xdt = MUON_BF16;
   int ts = 256;
   int waves = 4;
-  int order = 1;   // plain block order: per-XCD tile ranges unbalance mixed-cost groups
+  // block order per phase (GRAM, POLY, APPLY): bit 0 plain order (no per-XCD
+  // tile ranges), bit 1 row-major APPLY tiles (else groups of four row panels)
+  int order[3] = {1, 1, 1};
+  std::vector<int> launch_groups;   // groups in launch order: costliest tiles first
   std::vector<GroupPlan> groups;
   std::vector<int> mat_group, mat_slot;
   size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
@@ -123,7 +128,6 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   p.waves = (p.ts == 256 && xdt == MUON_BF16) ? 8 : 4;
   if (const char* e = std::getenv("MUON_WAVES"))
     if (std::atoi(e) == 4) p.waves = 4;
-  if (const char* e = std::getenv("MUON_GEMM_ORDER")) p.order = std::atoi(e) & 3;
 
   const int es = esize(xdt);
   size_t off = 0;
@@ -150,6 +154,25 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
     g.off_part = off; off = align_up(off + cnt * size_t(g.npart) * 4, kAlign);
   }
   p.total = off;
+  // APPLY: when matrices are small (few tiles each) give every XCD a
+  // contiguous range of tiles, row-major, so whole matrices stay in one L2;
+  // large matrices run in plain block order with four-row-panel groups
+  {
+    int64_t tiles = 0;
+    for (auto& g : p.groups) tiles += int64_t(g.mats.size()) * (g.mp / p.ts) * (g.np / p.ts);
+    p.order[2] = (n > 0 && tiles <= int64_t(40) * n) ? 2 : 1;
+  }
+  // MUON_GEMM_ORDER="g,p,a" overrides the per-phase order bits (experiments)
+  if (const char* e = std::getenv("MUON_GEMM_ORDER")) {
+    int v[3] = {p.order[0], p.order[1], p.order[2]};
+    if (std::sscanf(e, "%d,%d,%d", &v[0], &v[1], &v[2]) == 3)
+      for (int k = 0; k < 3; ++k) p.order[k] = v[k] & 3;
+  }
+  p.launch_groups.resize(p.groups.size());
+  for (size_t g = 0; g < p.groups.size(); ++g) p.launch_groups[g] = int(g);
+  std::stable_sort(p.launch_groups.begin(), p.launch_groups.end(), [&](int a, int b) {
+    return p.groups[a].np > p.groups[b].np;
+  });
   p.pprefix.assign(n + 1, 0);
   p.fprefix.assign(n + 1, 0);
   for (int i = 0; i < n; ++i) {
@@ -161,7 +184,7 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
 
 // Plans cached by (shape list, iterate type, tile override).
 std::mutex g_mu;
-std::map<std::tuple<std::vector<int64_t>, int, int>, Plan> g_plans;
+std::map<std::tuple<std::vector<int64_t>, int, std::string>, Plan> g_plans;
 
 const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   std::vector<int64_t> key(2 * size_t(n));
@@ -169,7 +192,7 @@ const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   const char* e = std::getenv("MUON_TILE");
   const char* w = std::getenv("MUON_WAVES");
   const char* o = std::getenv("MUON_GEMM_ORDER");
-  const int tile_env = ((e ? std::atoi(e) : 0) * 16 + (w ? std::atoi(w) : 0)) * 4 + (o ? std::atoi(o) & 3 : 0);
+  const std::string tile_env = std::string(e ? e : "-") + "/" + (w ? w : "-") + "/" + (o ? o : "-");
   auto k = std::make_tuple(std::move(key), xdt, tile_env);
   auto it = g_plans.find(k);
   if (it != g_plans.end()) return it->second;
@@ -317,7 +340,6 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
     ga.ca = a; ga.cb = b; ga.cc = c;
     ga.cbb = poly ? 1.f : b;
     ga.eps = eps;
-    ga.order = p.order;
     const int es = esize(p.xdt);
     // groups are processed in launch sets of at most kMaxGroups
     for (size_t g0 = 0; g0 < p.groups.size(); g0 += kMaxGroups) {
@@ -326,8 +348,9 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
         if (phase == 1 && !poly) continue;
         int64_t blocks = 0;
         ga.ngroups = int(g1 - g0);
+        ga.order = p.order[phase];
         for (size_t gi = g0; gi < g1; ++gi) {
-          const GroupPlan& g = p.groups[gi];
+          const GroupPlan& g = p.groups[p.launch_groups[gi]];
           GemmGroup& d = ga.g[gi - g0];
           const int tm = g.mp / p.ts, tn = g.np / p.ts;
           char* xin = ws + (cur ? g.off_x1 : g.off_x0);

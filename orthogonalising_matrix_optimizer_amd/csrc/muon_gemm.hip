@@ -31,6 +31,8 @@
 // off-diagonal tiles also store their mirror image.  The MFMA output layout
 // gives each lane four consecutive rows of one column; the tiles are arranged
 // so that those four values are contiguous in memory (row Q, columns P..P+3).
+#include <type_traits>
+
 #include "muon_common.h"
 
 namespace muon {
@@ -86,15 +88,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 // Four consecutive elements <-> floats.
-__device__ __forceinline__ void ld4(const uint16_t* p, float* v) {
-  const uint2 q = *reinterpret_cast<const uint2*>(p);
+__device__ __forceinline__ void unpack4(const uint2 q, float* v) {
   v[0] = __uint_as_float(q.x << 16);
   v[1] = __uint_as_float(q.x & 0xffff0000u);
   v[2] = __uint_as_float(q.y << 16);
   v[3] = __uint_as_float(q.y & 0xffff0000u);
 }
-__device__ __forceinline__ void ld4(const float* p, float* v) {
-  const float4 q = *reinterpret_cast<const float4*>(p);
+__device__ __forceinline__ void unpack4(const float4 q, float* v) {
   v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
 }
 __device__ __forceinline__ void st4(uint16_t* p, const float* v) {
@@ -472,6 +472,26 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   const int ld_out = MODE == APPLY ? G.np : G.mp;
   const float alpha = MODE == GRAM ? scale * scale : 1.f;
   const bool mirror = MODE != APPLY && tP != tQ;
+  // POLY and APPLY add a multiple of their input at the output positions:
+  // load all of this lane's input values first, so the loads overlap each
+  // other instead of each store waiting for its own load
+  constexpr int NV = MODE == GRAM ? 1 : FP * FQ * 4;
+  using V4 = typename std::conditional<XDT == kBF16, uint2, float4>::type;
+  V4 pre[NV];
+  if constexpr (MODE != GRAM) {
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) {
+        const int Q = tQ * TS + wc * WTQ + j * 32 + (lane & 31);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int P = tP * TS + wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
+          pre[(i * FQ + j) * 4 + rg] =
+              *reinterpret_cast<const V4*>(xin + static_cast<int64_t>(Q) * ld_out + P);
+        }
+      }
+  }
 #pragma unroll
   for (int i = 0; i < FP; ++i) {
 #pragma unroll
@@ -484,19 +504,19 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][rg * 4 + e];
         const int64_t qp = static_cast<int64_t>(Q) * ld_out + P;
-        if (MODE == GRAM) {
+        if constexpr (MODE == GRAM) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= alpha;
-        } else if (MODE == POLY) {
-          float av[4];
-          ld4(xin + qp, av);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = args.cb * av[e] + args.cc * v[e];
         } else {
           float xv[4];
-          ld4(xin + qp, xv);
+          unpack4(pre[(i * FQ + j) * 4 + rg], xv);
+          if constexpr (MODE == POLY) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = scale * (args.ca * xv[e] + args.cbb * v[e]);
+            for (int e = 0; e < 4; ++e) v[e] = args.cb * xv[e] + args.cc * v[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = scale * (args.ca * xv[e] + args.cbb * v[e]);
+          }
         }
         st4(out + qp, v);
         if (mirror) {
