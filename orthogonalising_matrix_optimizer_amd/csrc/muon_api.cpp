@@ -47,7 +47,8 @@ struct Plan {
   int ts = 256;
   int waves = 4;
   // block order per phase (GRAM, POLY, APPLY): bit 0 plain order (no per-XCD
-  // tile ranges), bit 1 row-major APPLY tiles (else groups of four row panels)
+  // tile ranges), bit 1 row-major APPLY tiles (else groups of four row
+  // panels), bit 2 whole matrices dealt to XCDs (matrix j on XCD j mod 8)
   int order[3] = {1, 1, 1};
   std::vector<int> launch_groups;   // groups in launch order: costliest tiles first
   std::vector<GroupPlan> groups;
@@ -55,6 +56,27 @@ struct Plan {
   size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
   std::vector<int64_t> pprefix, fprefix;
 };
+
+// Whether dealing whole matrices to the eight XCDs (matrix j of every group
+// on XCD j mod 8) gives each XCD within 5% of the mean work in every launch
+// set of a symmetric phase (0 GRAM, 1 POLY).
+bool xcd_deal_balanced(const Plan& p, int phase) {
+  for (size_t g0 = 0; g0 < p.groups.size(); g0 += kMaxGroups) {
+    const size_t g1 = std::min(p.groups.size(), g0 + kMaxGroups);
+    double cost[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tot = 0;
+    for (size_t gi = g0; gi < g1; ++gi) {
+      const GroupPlan& g = p.groups[p.launch_groups[gi]];
+      const int tm = g.mp / p.ts;
+      const double unit = double(tm) * (tm + 1) / 2 * (phase == 0 ? g.np : g.mp);
+      const int c = int(g.mats.size());
+      for (int x = 0; x < 8; ++x) cost[x] += ((c + 7 - x) / 8) * unit;
+      tot += c * unit;
+    }
+    for (int x = 0; x < 8; ++x)
+      if (cost[x] > 1.05 * tot / 8) return false;
+  }
+  return true;
+}
 
 // Relative throughput of a tile edge (larger tiles reuse operands more).
 double tile_eff(int ts) { return ts == 256 ? 1.0 : ts == 128 ? 0.75 : 0.45; }
@@ -162,17 +184,21 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
     for (auto& g : p.groups) tiles += int64_t(g.mats.size()) * (g.mp / p.ts) * (g.np / p.ts);
     p.order[2] = (n > 0 && tiles <= int64_t(40) * n) ? 2 : 1;
   }
-  // MUON_GEMM_ORDER="g,p,a" overrides the per-phase order bits (experiments)
-  if (const char* e = std::getenv("MUON_GEMM_ORDER")) {
-    int v[3] = {p.order[0], p.order[1], p.order[2]};
-    if (std::sscanf(e, "%d,%d,%d", &v[0], &v[1], &v[2]) == 3)
-      for (int k = 0; k < 3; ++k) p.order[k] = v[k] & 3;
-  }
   p.launch_groups.resize(p.groups.size());
   for (size_t g = 0; g < p.groups.size(); ++g) p.launch_groups[g] = int(g);
   std::stable_sort(p.launch_groups.begin(), p.launch_groups.end(), [&](int a, int b) {
     return p.groups[a].np > p.groups[b].np;
   });
+  // GRAM and POLY: whole matrices per XCD when that keeps the XCDs balanced
+  // (tiles of one matrix share operand panels in that XCD's L2)
+  for (int ph = 0; ph < 2; ++ph)
+    if (xcd_deal_balanced(p, ph)) p.order[ph] = 4;
+  // MUON_GEMM_ORDER="g,p,a" overrides the per-phase order bits (experiments)
+  if (const char* e = std::getenv("MUON_GEMM_ORDER")) {
+    int v[3] = {p.order[0], p.order[1], p.order[2]};
+    if (std::sscanf(e, "%d,%d,%d", &v[0], &v[1], &v[2]) == 3)
+      for (int k = 0; k < 3; ++k) p.order[k] = v[k] & 7;
+  }
   p.pprefix.assign(n + 1, 0);
   p.fprefix.assign(n + 1, 0);
   for (int i = 0; i < n; ++i) {
@@ -379,6 +405,14 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
         (void)es;
         const int ph = phase == 0 ? MUON_PHASE_GRAM : phase == 1 ? MUON_PHASE_POLY : MUON_PHASE_APPLY;
         probe_begin(ph, s);
+        if (ga.order & 4) {
+          // every XCD gets as many blocks as the one with the most matrices;
+          // the surplus blocks of the others exit at once
+          int64_t per = 0;
+          for (int k = 0; k < ga.ngroups; ++k)
+            per += int64_t((ga.g[k].count + 7) / 8) * ga.g[k].tiles;
+          blocks = 8 * per;
+        }
         hipError_t err = launch_gemm(phase, p.xdt, p.ts, p.waves, ga, blocks, s);
         probe_end(ph, s);
         if (err != hipSuccess) return err;

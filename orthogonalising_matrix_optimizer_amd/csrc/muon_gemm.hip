@@ -13,20 +13,20 @@
 //
 // Tiling: square TS x TS output tiles, a WGP x WGQ grid of waves, each wave
 // a sub-tile of 32x32 MFMA blocks.  Every operand tile goes from global memory
-// to LDS by buffer loads with the LDS-DMA bit (no register staging) into a
-// ring of four LDS stages, each holding 64 bytes of contraction per operand
-// row; loads run three stages ahead of the MFMAs, one barrier per stage.
-//   * Operands whose contraction index is contiguous in memory (both GRAM
-//     operands, both POLY operands, the B operand of APPLY) are stored as
-//     64-byte rows of four 16-byte chunks, the chunk index XOR-ed with
-//     (row >> 1) & 3, so the 8 rows read by each 8-lane slice of an MFMA
-//     operand load cover all banks.
-//   * APPLY contracts over the rows of X, so its X tile is stored row-major
-//     (contraction index = LDS row, chunk index XOR-ed with 2 (row & 3)) and
-//     the bf16 MFMA operand is assembled by the LDS transpose read (each
-//     16-lane group turns a 4 x 16 block into four consecutive contraction
-//     values per column; its four rows land on four distinct 32-byte bank
-//     slots).
+// to LDS by buffer loads with the LDS-DMA bit (no register staging).
+//   * bf16: two LDS stages of 128 bytes of contraction per operand row (one
+//     full cache line per row and load), the next stage loading while the
+//     current one is multiplied; one barrier per stage.
+//   * fp32: a ring of four stages of 64 bytes per row, loads three stages
+//     ahead.
+// Operands whose contraction index is contiguous in memory (both GRAM
+// operands, both POLY operands, the B operand of APPLY) are stored as rows of
+// 16-byte chunks with the chunk index XOR-ed with a function of the row, so
+// the 16 rows read by each 16-lane slice of an MFMA operand load cover all 64
+// banks.  APPLY contracts over the rows of X, so its X tile is stored
+// row-major (contraction index = LDS row) and the bf16 MFMA operand is
+// assembled by the LDS transpose read (each 16-lane group turns a 4 x 16
+// block into four consecutive contraction values per column).
 // GRAM and POLY are symmetric: only tiles on or above the diagonal run, and
 // off-diagonal tiles also store their mirror image.  The MFMA output layout
 // gives each lane four consecutive rows of one column; the tiles are arranged
@@ -48,28 +48,34 @@ enum { GRAM = 0, POLY = 1, APPLY = 2 };
 
 // Buffer descriptor word 3 for raw (untyped) loads.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
-constexpr int kStages = 4;
-
 template <int XDT> struct Ty;
 template <> struct Ty<kBF16> {
   using T = uint16_t;
-  static constexpr int ES = 2;   // element bytes
-  static constexpr int BK = 32;  // contraction elements per stage (64-byte rows)
+  static constexpr int ES = 2;    // element bytes
+  static constexpr int BK = 64;   // contraction elements per stage (128-byte rows)
+  static constexpr int CPR = 8;   // 16-byte chunks per operand row per stage
+  static constexpr int NST = 2;   // LDS stages
 };
 template <> struct Ty<kF32> {
   using T = float;
   static constexpr int ES = 4;
   static constexpr int BK = 16;
+  static constexpr int CPR = 4;
+  static constexpr int NST = 4;
 };
 
 // LDS bank model: 64 four-byte banks; a 16-byte-per-lane read is served 16
 // lanes (256 bytes) at a time, an 8-byte read 32 lanes at a time.
 //
-// K-contiguous tile: row r, logical 16-byte chunk c (0..3).  Four rows share
-// a 256-byte bank line; XOR-ing the chunk with (r >> 2) & 3 puts the 16 rows
-// read by one 16-lane slice on 16 distinct 16-byte slots.
+// K-contiguous tile: row r, logical 16-byte chunk c.  With four chunks per
+// row (64 bytes) four rows share a 256-byte bank line and the chunk is XOR-ed
+// with (r >> 2) & 3; with eight (128 bytes) two rows share a line and the
+// chunk is XOR-ed with (r >> 1) & 7.  Either way the 16 rows read by one
+// 16-lane slice land on 16 distinct 16-byte slots.
+template <int CPR>
 __device__ __forceinline__ int kc_off(int r, int c) {
-  return (r << 6) + ((c ^ ((r >> 2) & 3)) << 4);
+  if constexpr (CPR == 4) return (r << 6) + ((c ^ ((r >> 2) & 3)) << 4);
+  else return (r << 7) + ((c ^ ((r >> 1) & 7)) << 4);
 }
 // Row-major X tile: contraction row k, column p.  The chunk index is XOR-ed
 // with 4 (k & 3), so the four rows read by two transpose groups (64 bytes
@@ -189,19 +195,28 @@ struct OpLoad {
   uint32_t ld_bytes;
 };
 
-// K-contiguous operand: instruction j moves rows 16j..16j+15 (1 KiB); lane L
-// fills physical chunk L & 3 of row 16j + L/4 with the logical chunk the
-// swizzle maps there, (L & 3) ^ ((L >> 4) & 3) for every j.
-__device__ __forceinline__ void plan_kc(OpLoad& o, int lane) {
-  o.voff = static_cast<uint32_t>(lane >> 2) * o.ld_bytes + 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+// K-contiguous operand, one 1 KiB instruction j per 64 / CPR rows.  Four
+// chunks: rows 16j..16j+15, lane L fills physical chunk L & 3 of row
+// 16j + L/4 with logical chunk (L & 3) ^ ((L >> 4) & 3) for every j.  Eight
+// chunks: rows 8j..8j+7, lane L fills physical chunk L & 7 of row 8j + L/8
+// with logical chunk (L & 7) ^ ((4 (j & 1) + L/16) & 7); j = wave (mod 2)
+// because the wave count is even, so the offset is fixed per lane.
+template <int CPR>
+__device__ __forceinline__ void plan_kc(OpLoad& o, int lane, int wave) {
+  if constexpr (CPR == 4)
+    o.voff = static_cast<uint32_t>(lane >> 2) * o.ld_bytes + 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+  else
+    o.voff = static_cast<uint32_t>(lane >> 3) * o.ld_bytes +
+             16u * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
 }
 
-template <int TS, int NW>
+template <int TS, int NW, int CPR>
 __device__ __forceinline__ void load_kc(const OpLoad& o, uint32_t kbytes, int wave, uint8_t* dst) {
+  constexpr int RPI = 64 / CPR;
 #pragma unroll
-  for (int u = 0; u < TS / (16 * NW); ++u) {
+  for (int u = 0; u < TS / (RPI * NW); ++u) {
     const int j = wave + NW * u;
-    dma16(o.rs, lds_addr(dst) + j * 1024, o.voff, o.origin + 16u * j * o.ld_bytes + kbytes);
+    dma16(o.rs, lds_addr(dst) + j * 1024, o.voff, o.origin + RPI * j * o.ld_bytes + kbytes);
   }
 }
 
@@ -232,7 +247,7 @@ __device__ __forceinline__ void load_rm(const OpLoad& o, uint32_t k0, int wave, 
 
 // MFMA over one LDS stage; the wave at (wr, wc) of a WGP x WGQ grid owns a
 // (TS/WGP) x (TS/WGQ) sub-tile made of FP x FQ 32x32 blocks.
-template <int XDT, int MODE, int TS, int WGP, int WGQ>
+template <int XDT, int MODE, int TS, int WGP, int WGQ, int H>
 __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* sbp, int lane,
                                              int wr, int wc,
                                              f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
@@ -249,7 +264,7 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
 #pragma unroll
       for (int f = 0; f < FP; ++f) {
         if constexpr (MODE == APPLY) {
-          const int kb = 16 * kk + 8 * (g >> 1) + (i >> 2);
+          const int kb = 32 * H + 16 * kk + 8 * (g >> 1) + (i >> 2);
           const int p = wr * WTP + f * 32 + 16 * (g & 1) + 4 * (i & 3);
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_i16x4_t*)(sa + rm_off<TS, 2>(kb, p)));
@@ -257,12 +272,12 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
               (lds_i16x4_t*)(sa + rm_off<TS, 2>(kb + 4, p)));
           fa[kk][f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-          fa[kk][f] = *reinterpret_cast<const bf16x8_t*>(sa + kc_off(wr * WTP + f * 32 + l32, 2 * kk + hl));
+          fa[kk][f] = *reinterpret_cast<const bf16x8_t*>(sa + kc_off<8>(wr * WTP + f * 32 + l32, 4 * H + 2 * kk + hl));
         }
       }
 #pragma unroll
       for (int f = 0; f < FQ; ++f)
-        fb[kk][f] = *reinterpret_cast<const bf16x8_t*>(sbp + kc_off(wc * WTQ + f * 32 + l32, 2 * kk + hl));
+        fb[kk][f] = *reinterpret_cast<const bf16x8_t*>(sbp + kc_off<8>(wc * WTQ + f * 32 + l32, 4 * H + 2 * kk + hl));
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -292,8 +307,8 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
 #pragma unroll
     for (int f = 0; f < FQ; ++f) {
       const int rb_ = wc * WTQ + f * 32 + l32;
-      const float4 b0 = *reinterpret_cast<const float4*>(sbp + kc_off(rb_, 2 * hl));
-      const float4 b1 = *reinterpret_cast<const float4*>(sbp + kc_off(rb_, 2 * hl + 1));
+      const float4 b0 = *reinterpret_cast<const float4*>(sbp + kc_off<4>(rb_, 2 * hl));
+      const float4 b1 = *reinterpret_cast<const float4*>(sbp + kc_off<4>(rb_, 2 * hl + 1));
       fb[f][0] = b0.x; fb[f][1] = b0.y; fb[f][2] = b0.z; fb[f][3] = b0.w;
       fb[f][4] = b1.x; fb[f][5] = b1.y; fb[f][6] = b1.z; fb[f][7] = b1.w;
     }
@@ -306,8 +321,8 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
           fa[f][s] = *reinterpret_cast<const float*>(sa + rm_off<TS, 4>(8 * hl + s, p));
       } else {
         const int ra_ = wr * WTP + f * 32 + l32;
-        const float4 a0 = *reinterpret_cast<const float4*>(sa + kc_off(ra_, 2 * hl));
-        const float4 a1 = *reinterpret_cast<const float4*>(sa + kc_off(ra_, 2 * hl + 1));
+        const float4 a0 = *reinterpret_cast<const float4*>(sa + kc_off<4>(ra_, 2 * hl));
+        const float4 a1 = *reinterpret_cast<const float4*>(sa + kc_off<4>(ra_, 2 * hl + 1));
         fa[f][0] = a0.x; fa[f][1] = a0.y; fa[f][2] = a0.z; fa[f][3] = a0.w;
         fa[f][4] = a1.x; fa[f][5] = a1.y; fa[f][6] = a1.z; fa[f][7] = a1.w;
       }
@@ -326,33 +341,39 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
 template <int XDT, int MODE, int TS, int NW>
 __device__ __forceinline__ void gemm_issue(const OpLoad& la, const OpLoad& lb, int k, int wave,
                                            uint8_t* dst) {
-  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, OPB = TS * 64;
+  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, OPB = TS * CPR * 16;
   const uint32_t k0 = static_cast<uint32_t>(k) * BK;
   if constexpr (MODE == APPLY) load_rm<TS, ES, BK, NW>(la, k0, wave, dst);
-  else load_kc<TS, NW>(la, k0 * ES, wave, dst);
-  load_kc<TS, NW>(lb, k0 * ES, wave, dst + OPB);
+  else load_kc<TS, NW, CPR>(la, k0 * ES, wave, dst);
+  load_kc<TS, NW, CPR>(lb, k0 * ES, wave, dst + OPB);
 }
 
-// One stage: wait for stage k, refill the buffer of stage k-1 with stage k+3,
-// multiply from stage k.
+// One stage: wait for stage k, refill the buffer of stage k-1 with stage
+// k + NST - 1, multiply from stage k.
 template <int XDT, int MODE, int TS, int WGP, int WGQ>
 __device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, int k, int nk,
                                           int wave, int lane, int wr, int wc, uint8_t* cur,
                                           uint8_t* fill,
                                           f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
-  constexpr int NW = WGP * WGQ, OPB = TS * 64;
-  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK;
-  constexpr int NA = MODE == APPLY ? BK / (1024 / (TS * ES)) / NW : TS / (16 * NW);
-  constexpr int PER = NA + TS / (16 * NW);   // loads per wave per stage
-  const int ahead = nk - 1 - k;              // stages issued after this one: min(2, ahead)
-  if (ahead >= 2) wait_vm<2 * PER>();
-  else if (ahead == 1) wait_vm<PER>();
-  else wait_vm<0>();
+  constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, NST = Ty<XDT>::NST;
+  constexpr int NW = WGP * WGQ, OPB = TS * CPR * 16, RPI = 64 / CPR;
+  constexpr int NA = MODE == APPLY ? BK / (1024 / (TS * ES)) / NW : TS / (RPI * NW);
+  constexpr int PER = NA + TS / (RPI * NW);   // loads per wave per stage
+  if constexpr (NST == 4) {
+    const int ahead = nk - 1 - k;             // stages issued after this one: min(2, ahead)
+    if (ahead >= 2) wait_vm<2 * PER>();
+    else if (ahead == 1) wait_vm<PER>();
+    else wait_vm<0>();
+  } else {
+    wait_vm<0>();
+  }
   // bare barrier: a fenced __syncthreads would also wait for the loads of the
   // stages still in flight
   lds_barrier();
-  if (k + 3 < nk) gemm_issue<XDT, MODE, TS, NW>(la, lb, k + 3, wave, fill);
-  gemm_compute<XDT, MODE, TS, WGP, WGQ>(cur, cur + OPB, lane, wr, wc, acc);
+  if (k + NST - 1 < nk) gemm_issue<XDT, MODE, TS, NW>(la, lb, k + NST - 1, wave, fill);
+  gemm_compute<XDT, MODE, TS, WGP, WGQ, 0>(cur, cur + OPB, lane, wr, wc, acc);
+  if constexpr (XDT == kBF16)
+    gemm_compute<XDT, MODE, TS, WGP, WGQ, 1>(cur, cur + OPB, lane, wr, wc, acc);
 }
 
 // Logical block index: blocks are dealt round-robin to the eight XCDs; this
@@ -368,28 +389,56 @@ template <int XDT, int MODE, int TS, int WGP, int WGQ>
 __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   using T = typename Ty<XDT>::T;
   constexpr int ES = Ty<XDT>::ES;
-  constexpr int BK = Ty<XDT>::BK;
+  constexpr int BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, NST = Ty<XDT>::NST;
   constexpr int NW = WGP * WGQ;       // waves per block
   constexpr int WTP = TS / WGP, WTQ = TS / WGQ;
   constexpr int FP = WTP / 32, FQ = WTQ / 32;
-  constexpr int OPB = TS * 64;        // LDS bytes per operand per stage
+  constexpr int OPB = TS * CPR * 16;  // LDS bytes per operand per stage
 
-  __shared__ __attribute__((aligned(1024))) uint8_t sm0[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm1[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm2[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm3[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * 2 * OPB];
+  uint8_t* const sm0 = smem;
+  uint8_t* const sm1 = smem + 2 * OPB;
+  uint8_t* const sm2 = smem + (NST > 2 ? 4 : 0) * OPB;
+  uint8_t* const sm3 = smem + (NST > 2 ? 6 : 2) * OPB;
   __shared__ float red[NW];
 
   // ---- locate group, matrix and tile
-  const int bid = (args.order & 1) ? static_cast<int>(blockIdx.x) : xcd_block();
-  // constant-index selection keeps the group table in kernel-argument space
   GemmGroup G = args.g[0];
+  int mat, tile;
+  if (args.order & 4) {
+    // matrices dealt to XCDs: matrix j of every group runs on XCD j mod 8;
+    // block b is the (b / 8)-th block dispatched to XCD b mod 8
+    const int x = static_cast<int>(blockIdx.x & 7);
+    int i = static_cast<int>(blockIdx.x >> 3);
+    int found = 0;
+    mat = 0; tile = 0;
 #pragma unroll
-  for (int k = 1; k < kMaxGroups; ++k)
-    if (k < args.ngroups && bid >= args.g[k].block_base) G = args.g[k];
-  const int local = bid - G.block_base;
-  const int mat = local / G.tiles;
-  const int tile = local - mat * G.tiles;
+    for (int k = 0; k < kMaxGroups; ++k) {
+      if (k < args.ngroups && !found) {
+        const int n = (args.g[k].count + 7 - x) >> 3;
+        const int nb = n * args.g[k].tiles;
+        if (i < nb) {
+          G = args.g[k];
+          const int jm = i / G.tiles;
+          mat = x + 8 * jm;
+          tile = i - jm * G.tiles;
+          found = 1;
+        } else {
+          i -= nb;
+        }
+      }
+    }
+    if (!found) return;
+  } else {
+    const int bid = (args.order & 1) ? static_cast<int>(blockIdx.x) : xcd_block();
+    // constant-index selection keeps the group table in kernel-argument space
+#pragma unroll
+    for (int k = 1; k < kMaxGroups; ++k)
+      if (k < args.ngroups && bid >= args.g[k].block_base) G = args.g[k];
+    const int local = bid - G.block_base;
+    mat = local / G.tiles;
+    tile = local - mat * G.tiles;
+  }
   int tP, tQ;
   if (MODE == APPLY && (args.order & 2)) {
     tP = tile % (G.np / TS);
@@ -427,8 +476,8 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
     la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
     la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
     lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
-    plan_kc(la, lane);
-    plan_kc(lb, lane);
+    plan_kc<CPR>(la, lane, wave);
+    plan_kc<CPR>(lb, lane, wave);
   } else {
     K = G.mp;
     la.rs = make_desc(xin, static_cast<uint32_t>(G.mp) * G.np * ES);
@@ -439,7 +488,7 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
     lb.rs = make_desc(bm, static_cast<uint32_t>(G.mp) * G.mp * ES);
     lb.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
     lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
-    plan_kc(lb, lane);
+    plan_kc<CPR>(lb, lane, wave);
   }
 
   float scale = 1.f;
@@ -455,17 +504,26 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // the planner pads every dimension to a multiple of 128, so nk is a
-  // multiple of four and each trip below runs the four ring buffers in order
+  // multiple of the stage count and each trip below runs the buffers in order
   const int nk = K / BK;
-  gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
-  gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1);
-  gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2);
+  if constexpr (NST == 4) {
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2);
 #pragma unroll 1
-  for (int kt = 0; kt < nk; kt += kStages) {
-    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, acc);
-    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
-    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, acc);
-    gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, acc);
+    for (int kt = 0; kt < nk; kt += 4) {
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, acc);
+    }
+  } else {
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
+#pragma unroll 1
+    for (int kt = 0; kt < nk; kt += 2) {
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm1, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+    }
   }
 
   // ---- epilogue
