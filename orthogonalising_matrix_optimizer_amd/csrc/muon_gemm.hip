@@ -376,6 +376,137 @@ __device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, in
     gemm_compute<XDT, MODE, TS, WGP, WGQ, 1>(cur, cur + OPB, lane, wr, wc, acc);
 }
 
+// ---- input term and staged output of 256-wide bf16 tiles
+//
+// POLY (B = b A + c A A) and APPLY (X' = s (a X + beta B X)) add a multiple of
+// their input at the output positions.  That input tile passes through LDS
+// during the K loop anyway (APPLY: rows Q of X are the contraction rows of one
+// stage; POLY: A[Q][P] = A[P][Q] is part of the stage whose contraction range
+// covers P), so each wave folds coef * input into its accumulators there:
+// acc = product + coef * input, output = mult * acc, with coef = a / beta,
+// mult = s beta (APPLY) and coef = b / c, mult = c (POLY).
+template <int MODE, int TS, int WGP, int WGQ>
+__device__ __forceinline__ void capture_input(int k, const uint8_t* stage, int lane, int wr,
+                                              int wc, int tP, int tQ, float coef,
+                                              f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
+  constexpr int WTP = TS / WGP, WTQ = TS / WGQ, FP = WTP / 32, FQ = WTQ / 32;
+  constexpr int BK = Ty<kBF16>::BK, OPB = TS * Ty<kBF16>::CPR * 16;
+  const int k0 = k * BK;
+  if constexpr (MODE == APPLY) {
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int q0 = tQ * TS + wc * WTQ + j * 32;   // first X row of fragment j
+      if (q0 >= k0 && q0 < k0 + BK) {
+        const int r = q0 - k0 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < FP; ++i)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int p = wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
+            float x[4];
+            unpack4(*reinterpret_cast<const uint2*>(stage + rm_off<TS, 2>(r, p)), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][rg * 4 + e] += coef * x[e];
+          }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FP; ++i) {
+      const int p0 = tP * TS + wr * WTP + i * 32;   // first column of fragment i
+      if (p0 >= k0 && p0 < k0 + BK) {
+#pragma unroll
+        for (int j = 0; j < FQ; ++j) {
+          const int row = wc * WTQ + j * 32 + (lane & 31);
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int kk = p0 - k0 + rg * 8 + (lane >> 5) * 4;
+            float x[4];
+            unpack4(*reinterpret_cast<const uint2*>(stage + OPB + kc_off<8>(row, kk >> 3) +
+                                                    (kk & 7) * 2), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][rg * 4 + e] += coef * x[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Staging tile of a 256 x 256 bf16 output in LDS: row Q (512 bytes), 8-byte
+// slot s = P / 4 stored at s ^ stg_sw(Q).  The 32 rows written by one
+// half-wave (same P) land on 32 distinct bank pairs, and the two slots of a
+// 16-byte chunk stay together (chunk c at c ^ (Q & 15), halves swapped when
+// bit 4 of Q is set).
+__device__ __forceinline__ int stg_sw(int q) { return (2 * (q & 15)) ^ ((q >> 4) & 1); }
+
+// Write mult * acc to the tile at (tQ, tP) through the LDS staging tile:
+// 16-byte row stores, and for off-diagonal GRAM/POLY tiles the mirror image
+// from transposing LDS reads (each 16-lane group turns 16 rows x 4 columns
+// into 4 rows x 16 columns).
+template <int MODE, int WGP, int WGQ>
+__device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_t ld, int tP,
+                                             int tQ, bool mirror, float mult, int wave, int lane,
+                                             int wr, int wc,
+                                             f32x16_t (&acc)[256 / WGP / 32][256 / WGQ / 32]) {
+  constexpr int TS = 256, NW = WGP * WGQ;
+  constexpr int WTP = TS / WGP, WTQ = TS / WGQ, FP = WTP / 32, FQ = WTQ / 32;
+  // every wave is past its last read of the stage buffers
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < FP; ++i)
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int q = wc * WTQ + j * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int p = wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
+        uint2 v;
+        v.x = static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4])) |
+              (static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4 + 1])) << 16);
+        v.y = static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4 + 2])) |
+              (static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4 + 3])) << 16);
+        *reinterpret_cast<uint2*>(stg + q * 512 + (((p >> 2) ^ stg_sw(q)) << 3)) = v;
+      }
+    }
+  __syncthreads();
+  // rows: two per instruction, 32 lanes x 16 bytes each
+#pragma unroll
+  for (int u = 0; u < TS / (2 * NW); ++u) {
+    const int q = 2 * (wave + NW * u) + (lane >> 5), c = lane & 31, sw = stg_sw(q);
+    uint4 v = *reinterpret_cast<const uint4*>(stg + q * 512 + ((c ^ (sw >> 1)) << 4));
+    if (sw & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(tQ * TS + q) * ld + tP * TS + 8 * c) = v;
+  }
+  if (!mirror) return;
+  // mirror: a pair of transposing reads gives lane j of group g eight
+  // consecutive rows Q0 + 8 (j / 4) + 0..7 of column 4 pq + j % 4, where the
+  // group's quad pq is qb + {0, 8, 1, 9}[g] (groups 0 and 1 read disjoint
+  // bank sets)
+  const int g = lane >> 4, i = lane & 15;
+  const int goff = (g & 1) * 8 + (g >> 1);
+#pragma unroll 4
+  for (int t = wave; t < 128; t += NW) {
+    const int n = t & 7, h = (t >> 3) & 3, m = t >> 5;
+    const int q0 = 32 * n, pq = 16 * m + 2 * h + goff;
+    i16x4_t r[2];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int q = q0 + 8 * (i & 3) + (i >> 2) + 4 * rr;
+      r[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(stg + q * 512 + ((pq ^ stg_sw(q)) << 3)));
+    }
+    const int p = 4 * pq + (i & 3);
+    uint4 v;
+    v.x = static_cast<uint16_t>(r[0][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[0][1])) << 16);
+    v.y = static_cast<uint16_t>(r[0][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[0][3])) << 16);
+    v.z = static_cast<uint16_t>(r[1][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[1][1])) << 16);
+    v.w = static_cast<uint16_t>(r[1][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[1][3])) << 16);
+    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(tP * TS + p) * ld + tQ * TS + q0 +
+                              8 * (i >> 2)) = v;
+  }
+}
+
 // Logical block index: blocks are dealt round-robin to the eight XCDs; this
 // gives each XCD a contiguous range of logical tiles, so tiles that share
 // operand panels run on the same L2.
@@ -503,6 +634,12 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // 256-wide bf16 tiles fold the input term in during the K loop and store
+  // through LDS (APPLY keeps the plain epilogue when beta == 0)
+  constexpr bool kStaged = XDT == kBF16 && TS == 256;
+  const bool capt = kStaged && (MODE == POLY || (MODE == APPLY && args.cbb != 0.f));
+  const float coef = MODE == POLY ? args.cb / args.cc : (capt ? args.ca / args.cbb : 0.f);
+
   // the planner pads every dimension to a multiple of 128, so nk is a
   // multiple of the stage count and each trip below runs the buffers in order
   const int nk = K / BK;
@@ -522,7 +659,11 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
 #pragma unroll 1
     for (int kt = 0; kt < nk; kt += 2) {
       gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm1, acc);
+      if constexpr (kStaged && MODE != GRAM)
+        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt, sm0, lane, wr, wc, tP, tQ, coef, acc);
       gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+      if constexpr (kStaged && MODE != GRAM)
+        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt + 1, sm1, lane, wr, wc, tP, tQ, coef, acc);
     }
   }
 
@@ -530,6 +671,14 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   const int ld_out = MODE == APPLY ? G.np : G.mp;
   const float alpha = MODE == GRAM ? scale * scale : 1.f;
   const bool mirror = MODE != APPLY && tP != tQ;
+  if constexpr (kStaged) {
+    if (MODE == GRAM || capt) {
+      const float mult = MODE == GRAM ? alpha : MODE == POLY ? args.cc : scale * args.cbb;
+      staged_store<MODE, WGP, WGQ>(smem, reinterpret_cast<uint16_t*>(out), ld_out, tP, tQ,
+                                   mirror, mult, wave, lane, wr, wc, acc);
+      return;
+    }
+  }
   // POLY and APPLY add a multiple of their input at the output positions:
   // load all of this lane's input values first, so the loads overlap each
   // other instead of each store waiting for its own load

@@ -77,6 +77,26 @@ def test_ragged_mixed_shapes(tile, ns, tol):
         assert sigma_dev(o, ref) <= TOL_SIGMA, u.shape
 
 
+@pytest.mark.parametrize("tile", [128, 256], indirect=True)
+@pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
+def test_mixed_coefficient_table(tile, ns, tol):
+    """A different polynomial per iteration: quintic, cubic (no A^2 term), a
+    purely linear step (b = c = 0: the product term vanishes) and quintic
+    again, on mixed shapes."""
+    announce(f"orthogonalize mixed coefficient table tile={tile} {ns}")
+    table = np.array([gen.QUINTIC, gen.CUBIC, (1.25, 0.0, 0.0), gen.QUINTIC, gen.CUBIC],
+                     dtype=np.float64)
+    shapes = [(300, 520), (520, 300), (256, 256), (100, 700)]
+    us = [gen.grad_matrix(r, c, 5, 0, i).astype(np.float32) for i, (r, c) in enumerate(shapes)]
+    ins = [dev_f32(u) for u in us]
+    outs = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in ins]
+    mo.orthogonalize(ins, outs, coeffs=table, steps=len(table), ns_dtype=ns)
+    torch.cuda.synchronize()
+    for u, o in zip(us, outs):
+        ref = orc.orthogonalize(u.astype(np.float64), table)
+        assert orc.rel_fro(host(o), ref) <= tol, u.shape
+
+
 def test_bf16_inputs_and_outputs():
     announce("orthogonalize bf16 in/out")
     shapes = [(96, 160), (160, 96), (128, 128)]
