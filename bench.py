@@ -9,8 +9,9 @@ Inputs are synthetic (seeded low-rank + noise gradients at entry RMS 1e-3,
 
 Prints one JSON line.  Extra fields: NS TFLOP/s (symmetric flop count),
 per-kernel times, the roofline of the dominant kernel (the APPLY GEMM,
-timed live with HIP events around its launches in the timed region) and the
-CPU oracle timed on the host on the same workload.
+timed live with HIP events around its launches in the timed region), the
+step replayed from one captured device graph, a single 256x512 matrix eager
+and replayed, and the CPU oracle timed on the host on the same workload.
 """
 from __future__ import annotations
 
@@ -86,6 +87,46 @@ def cpu_baseline(shapes, grads_bits, params_bits, coeffs, lr, wd, beta):
             "kind": "oracle",
             "sample": f"one full step of the same {len(shapes)}-matrix set on the host "
                       f"({dt:.2f} s, fp64 numpy/OpenBLAS)"}
+
+
+def _events_ms(fn, reps):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_graph(opt, grads, reps):
+    """ms per step of `opt` stepping on `grads` through one captured graph."""
+    import torch
+    g = opt.graph(grads)
+    g.replay()
+    torch.cuda.synchronize()
+    return round(_events_ms(g.replay, reps), 4)
+
+
+def single_matrix_times(gen, mo, dev, reps):
+    """One 256x512 fp32 matrix (five quintic iterations, bf16 operands): ms per
+    step eager and as a replayed graph."""
+    import torch
+    ms = gen.SETS["single_256x512"]
+    (g, w), = gen.make_inputs(ms, seed=0)
+    p = [torch.from_numpy(w).to(dev)]
+    gr = [torch.from_numpy(g).to(dev)]
+    opt = mo.Muon(p, lr=ms.lr, wd=ms.wd, beta=ms.beta, steps=ms.steps,
+                  coeffs=gen.coeff_table(ms.coeffs, ms.steps))
+    for _ in range(5):
+        opt.step(gr)
+    eager = _events_ms(lambda: opt.step(gr), max(reps, 20))
+    return {"workload": "one 256x512 fp32 matrix, 5 quintic iterations, bf16 operands",
+            "eager_ms_per_step": round(eager, 4),
+            "graph_ms_per_step": time_graph(opt, gr, max(reps, 20))}
 
 
 def main():
@@ -169,6 +210,12 @@ def main():
         phase_ms[ph] = round(float(np.mean(t)), 4) if t else None
     phase_ms["apply"] = round(float(np.mean(apply_ms)), 4) if apply_ms else None
 
+    # the same step captured once as a device graph and replayed (not part of
+    # `value`); and the single 256x512 fp32 matrix, eager and replayed, where
+    # launch latency dominates
+    graph_ms = time_graph(opt, grads, args.steps)
+    c1 = single_matrix_times(gen, mo, dev, args.steps)
+
     sym, dense = gen.ns_flops(shapes, ms.steps)
     a_flops = apply_flops(shapes)
     a_tf = a_flops / (phase_ms["apply"] * 1e-3) / 1e12
@@ -208,6 +255,8 @@ def main():
                      "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": a_flops, "launches_timed": len(apply_ms)},
         "wall_s_timed": round(wall, 4),
+        "graph_ms_per_step": graph_ms,
+        "single_matrix": c1,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, grads_bits, params_bits, coeffs, ms.lr,

@@ -59,7 +59,10 @@ enum {
   MUON_E_ALIAS = 7,      /* two buffers that must be distinct overlap          */
   MUON_E_ALIGN = 8,      /* a pointer or row pitch breaks 16-byte alignment    */
   MUON_E_HIP = 9,        /* a HIP runtime call failed                           */
-  MUON_E_STATE = 10      /* state inconsistent with the call (n, buffers)       */
+  MUON_E_STATE = 10,     /* state inconsistent with the call (n, buffers)       */
+  MUON_E_CAPTURE = 11    /* stream under graph capture, but the call's device
+                            descriptor table is not resident (see
+                            muon_step_prepare)                                 */
 };
 
 #define MUON_MAX_STEPS 16
@@ -135,6 +138,27 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n,
 int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
               const float* coeffs, int32_t steps, float lr, float wd,
               float beta, void* stream);
+
+/* Graph capture of a step (page "Training NanoGPT in 39.9 Seconds", Table A,
+ * credits capturing the training step as a device graph with part of the
+ * end-to-end gain).  muon_step enqueues only kernel launches, except that it
+ * first uploads a per-workspace descriptor table (matrix pointers, shapes,
+ * tile offsets) whenever that table changes, which synchronises the stream.
+ * muon_step_prepare validates the arguments exactly as muon_step does and
+ * makes that table resident for these params/grads/state buffers, without
+ * launching anything or touching the counters.  After it, a muon_step with
+ * the same buffers can be captured (hipStreamBeginCapture, or a framework's
+ * graph capture) on `stream`; a captured call whose table is not resident
+ * returns MUON_E_CAPTURE and enqueues nothing.
+ * A replay repeats the captured step on the same buffers with the captured
+ * scalars: lr, wd, beta, coefficients, options, and the weight-average flags
+ * derived from the counters (whether this step is averaged, and whether it is
+ * the first averaged step).  The capturing call advances step/ema_count once
+ * as for an eager call; replays do not touch the host state, so the caller
+ * advances the counters per replay and captures only steps whose flags repeat
+ * (weight average disabled, or already started).  Same errors as muon_step. */
+int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state* st,
+                      void* stream);
 
 /* Newton-Schulz part alone: out[i] = orthogonalise(in[i]) for n matrices
  * (same shapes; out may be any element type; in and out must not overlap).

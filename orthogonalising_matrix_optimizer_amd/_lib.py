@@ -13,6 +13,7 @@ STATUS = {
     0: "MUON_OK", 1: "MUON_E_NULL", 2: "MUON_E_SHAPE", 3: "MUON_E_DTYPE",
     4: "MUON_E_COEFFS", 5: "MUON_E_HPARAM", 6: "MUON_E_WORKSPACE",
     7: "MUON_E_ALIAS", 8: "MUON_E_ALIGN", 9: "MUON_E_HIP", 10: "MUON_E_STATE",
+    11: "MUON_E_CAPTURE",
 }
 CODES = {v: k for k, v in STATUS.items()}
 PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4}
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.muon_step.argtypes = [P(MuonMat), P(MuonMat), P(MuonState), P(c_float), c_int32,
                               c_float, c_float, c_float, c_void_p]
     lib.muon_step.restype = c_int32
+    lib.muon_step_prepare.argtypes = [P(MuonMat), P(MuonMat), P(MuonState), c_void_p]
+    lib.muon_step_prepare.restype = c_int32
     lib.muon_orthogonalize.argtypes = [P(MuonMat), P(MuonMat), c_int32, P(c_float), c_int32,
                                        P(MuonOptions), c_void_p, c_size_t, c_void_p]
     lib.muon_orthogonalize.restype = c_int32

@@ -236,27 +236,33 @@ struct Upload {
 };
 std::map<void*, Upload> g_uploads;
 
-hipError_t upload_table(void* ws, const std::vector<uint8_t>& bytes, hipStream_t s) {
+// A stream under graph capture cannot take the upload (it synchronises and
+// copies from a reused host buffer): the table must already be resident, put
+// there by muon_step_prepare or an eager call with the same buffers.
+int upload_table(void* ws, const std::vector<uint8_t>& bytes, hipStream_t s) {
   Upload& u = g_uploads[ws];
-  if (u.bytes == bytes) return hipSuccess;
+  if (u.bytes == bytes) return MUON_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MUON_E_HIP;
+  if (cs != hipStreamCaptureStatusNone) return MUON_E_CAPTURE;
   hipError_t err;
   if (u.pinned) {
     // the previous copy from this buffer may still be queued
-    if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;
+    if ((err = hipStreamSynchronize(s)) != hipSuccess) return MUON_E_HIP;
   }
   if (u.cap < bytes.size()) {
     if (u.pinned) (void)hipHostFree(u.pinned);
     u.pinned = nullptr;
     u.cap = 0;
     if ((err = hipHostMalloc(&u.pinned, bytes.size(), hipHostMallocDefault)) != hipSuccess)
-      return err;
+      return MUON_E_HIP;
     u.cap = bytes.size();
   }
   std::memcpy(u.pinned, bytes.data(), bytes.size());
   err = hipMemcpyAsync(ws, u.pinned, bytes.size(), hipMemcpyHostToDevice, s);
-  if (err != hipSuccess) { u.bytes.clear(); return err; }
+  if (err != hipSuccess) { u.bytes.clear(); return MUON_E_HIP; }
   u.bytes = bytes;
-  return hipSuccess;
+  return MUON_OK;
 }
 
 // ---------------------------------------------------------------- probes
@@ -454,6 +460,7 @@ const char* muon_status_str(int s) {
     case MUON_E_ALIGN: return "misaligned pointer";
     case MUON_E_HIP: return "HIP runtime error";
     case MUON_E_STATE: return "state inconsistent with the call";
+    case MUON_E_CAPTURE: return "descriptor table not resident for a call under stream capture";
     default: return "unknown status";
   }
 }
@@ -475,8 +482,11 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n, const muon_option
   return get_plan(rows.data(), cols.data(), n, xdt).total;
 }
 
-int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, const float* coeffs,
-              int32_t steps, float lr, float wd, float beta, void* stream) {
+namespace {
+// muon_step, or with prepare_only its validation and descriptor-table upload
+// alone (no launch, counters unchanged).
+int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, const float* coeffs,
+              int32_t steps, float lr, float wd, float beta, void* stream, bool prepare_only) {
   if (!st) return MUON_E_NULL;
   const int n = st->n;
   if (n < 0) return MUON_E_SHAPE;
@@ -487,6 +497,7 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   if ((rc = check_opt(o)) != MUON_OK) return rc;
   const bool ema_on = o.beta_ema >= 0.f && st->step + 1 >= o.ema_start;
   if (n == 0) {
+    if (prepare_only) return MUON_OK;
     st->step += 1;
     if (ema_on) st->ema_count += 1;
     return MUON_OK;
@@ -551,7 +562,8 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (upload_table(ws, bytes, s) != hipSuccess) return MUON_E_HIP;
+  if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
+  if (prepare_only) return MUON_OK;
 
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
@@ -592,6 +604,17 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   st->step += 1;
   if (ema_on) st->ema_count += 1;
   return MUON_OK;
+}
+}  // namespace
+
+int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, const float* coeffs,
+              int32_t steps, float lr, float wd, float beta, void* stream) {
+  return step_impl(params, grads, st, coeffs, steps, lr, wd, beta, stream, false);
+}
+
+int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state* st,
+                      void* stream) {
+  return step_impl(params, grads, st, nullptr, 0, 0.f, 0.f, 0.f, stream, true);
 }
 
 int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const float* coeffs,
@@ -643,7 +666,7 @@ int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (upload_table(ws, bytes, s) != hipSuccess) return MUON_E_HIP;
+  if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
   ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
@@ -715,7 +738,7 @@ int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (upload_table(ws, bytes, s) != hipSuccess) return MUON_E_HIP;
+  if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
   ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);

@@ -156,12 +156,28 @@ class Muon:
     def ema_count(self) -> int:
         return int(self.state.ema_count)
 
-    def step(self, grads: List[torch.Tensor], lr: Optional[float] = None,
-             wd: Optional[float] = None) -> None:
+    def _grad_mats(self, grads: List[torch.Tensor]):
         key = tuple((g.data_ptr(), g.stride(0), g.dtype) for g in grads)
         if key != self._gkey:
             self._gmats = _lib.mat_array(_mat(g) for g in grads)
             self._gkey = key
+        return self._gmats
+
+    def step_prepare(self, grads: List[torch.Tensor]) -> None:
+        """Make the device descriptor table for these gradient buffers resident
+        (no launch, counters unchanged), so a step with them can be captured."""
+        code = self.lib.muon_step_prepare(self._pmats, self._grad_mats(grads), self.state,
+                                          _stream())
+        _lib.check(code, "muon_step_prepare")
+
+    def graph(self, grads: List[torch.Tensor], lr: Optional[float] = None,
+              wd: Optional[float] = None) -> "StepGraph":
+        """Capture one step on `grads` as a device graph; see StepGraph."""
+        return StepGraph(self, grads, lr, wd)
+
+    def step(self, grads: List[torch.Tensor], lr: Optional[float] = None,
+             wd: Optional[float] = None) -> None:
+        self._grad_mats(grads)
         code = self.lib.muon_step(self._pmats, self._gmats, self.state, self._coeffs_c,
                                   self.steps, self.lr if lr is None else lr,
                                   self.wd if wd is None else wd, self.beta, _stream())
@@ -192,6 +208,47 @@ class Muon:
                 dst.copy_(src)
         self.state.step = int(sd["step"])
         self.state.ema_count = int(sd["ema_count"])
+
+
+class StepGraph:
+    """One optimizer step captured as a device graph and replayed.
+
+    The first replay performs the captured step; every replay repeats it on the
+    same buffers (parameters, the gradient tensors given at capture, state,
+    workspace) with the captured lr, wd, beta, coefficients and weight-average
+    flags.  Write new gradients into the captured gradient tensors before a
+    replay.  Host counters advance per replay as for an eager step.  Capture is
+    refused for a step whose weight-average flags would not repeat (the average
+    not yet started, or starting at this step): take eager steps first.
+    """
+
+    def __init__(self, opt: Muon, grads: List[torch.Tensor], lr: Optional[float] = None,
+                 wd: Optional[float] = None):
+        st, o = opt.state, opt.opt
+        if o.beta_ema >= 0.0:
+            if st.step + 1 < o.ema_start or st.ema_count == 0:
+                raise ValueError("capture after the weight average has started "
+                                 "(its first step re-initialises it)")
+        self.opt = opt
+        self.grads = list(grads)
+        self.ema_on = o.beta_ema >= 0.0
+        opt.step_prepare(self.grads)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            opt.step(self.grads, lr, wd)
+        # the capturing call advanced the counters for the step the first
+        # replay performs
+        self._pending = True
+
+    def replay(self) -> None:
+        self.g.replay()
+        if self._pending:
+            self._pending = False
+            return
+        self.opt.state.step += 1
+        if self.ema_on:
+            self.opt.state.ema_count += 1
 
 
 def ctypes_cast(a):

@@ -183,6 +183,26 @@ def test_rejects_missing_state(lib):
     assert _step(lib, p, g, st) == E["MUON_E_NULL"]
 
 
+def test_step_prepare_validates_like_step(lib):
+    """muon_step_prepare runs muon_step's validation (errors before any HIP
+    call) and never touches the counters."""
+    p, g, st, keep = _setup(lib, [(8, 16), (16, 8)])
+    need = st.workspace_bytes
+    st.workspace_bytes = need - 1
+    assert lib.muon_step_prepare(p, g, st, None) == E["MUON_E_WORKSPACE"]
+    st.workspace_bytes = need
+    g0 = g[0]
+    g[0] = _lib.MuonMat(p[0].ptr + 64, g0.rows, g0.cols, g0.ld, g0.dtype, 0)
+    assert lib.muon_step_prepare(p, g, st, None) == E["MUON_E_ALIAS"]
+    g[0] = g0
+    p2, g2, st2, keep2 = _setup(lib, [(8, 16)], beta_slow=0.99)
+    assert lib.muon_step_prepare(p2, g2, st2, None) == E["MUON_E_STATE"]
+    st.n = 0
+    assert lib.muon_step_prepare(p, g, st, None) == 0
+    assert st.step == 0 and st.ema_count == 0
+    assert lib.muon_step_prepare(p, g, None, None) == E["MUON_E_NULL"]
+
+
 def test_rejects_workspace_and_aliasing(lib):
     p, g, st, keep = _setup(lib, [(8, 16), (16, 8)])
     need = st.workspace_bytes

@@ -1,0 +1,96 @@
+"""Graph capture of the whole optimizer step: every replay against an eager
+twin optimizer on identical buffers, bit for bit (same kernels, same inputs,
+deterministic reductions), with eager device work and synchronisation
+between replays."""
+import pytest
+import torch
+
+import orthogonalising_matrix_optimizer_amd as mo
+from tests.gpu_helpers import announce
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(768, 3072), (3072, 768), (768, 768), (200, 333), (333, 200), (64, 1000)]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mo._lib.load()
+
+
+def _params(seed):
+    dev = torch.device("cuda")
+    return [gen.torch_param_matrix(r, c, seed, i, dev, dtype=torch.bfloat16)
+            for i, (r, c) in enumerate(SHAPES)]
+
+
+def _grads(seed, step):
+    dev = torch.device("cuda")
+    return [gen.torch_grad_matrix(r, c, seed, step, i, dev, rms=1e-3, dtype=torch.bfloat16)
+            for i, (r, c) in enumerate(SHAPES)]
+
+
+def _eager_work():
+    x = torch.randn(512, 512, device="cuda")
+    y = (x @ x).sum()
+    torch.cuda.synchronize()
+    return float(y)
+
+
+def _same(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def _run(kw, eager_first, replays):
+    pa = _params(7)
+    pb = [p.clone() for p in pa]
+    A = mo.Muon(pa, **kw)
+    B = mo.Muon(pb, **kw)
+    static = [torch.empty_like(g) for g in _grads(7, 0)]
+    t = 0
+    for _ in range(eager_first):
+        g = _grads(7, t)
+        A.step(g)
+        B.step(g)
+        t += 1
+    graph = B.graph(static)
+    for _ in range(replays):
+        g = _grads(7, t)
+        for dst, src in zip(static, g):
+            dst.copy_(src)
+        A.step(g)
+        _eager_work()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert _same(pa, pb), t
+        assert _same(A.mom, B.mom), t
+        if A.mom_slow is not None:
+            assert _same(A.mom_slow, B.mom_slow), t
+        if A.ema is not None:
+            assert _same(A.ema, B.ema), t
+        assert (A.step_count, A.ema_count) == (B.step_count, B.ema_count)
+        t += 1
+
+
+def test_graph_replays_match_eager_plain():
+    announce("graph: plain Muon, six replays")
+    _run(dict(lr=0.02, wd=0.01, beta=0.95, steps=5), eager_first=0, replays=6)
+
+
+def test_graph_replays_match_eager_anvil_ema():
+    announce("graph: fast/slow momentum, cautious decay, weight average")
+    kw = dict(lr=0.02, wd=0.1, beta=0.9, steps=6, beta_slow=0.99, cautious=True,
+              beta_ema=0.99, ema_start=1)
+    _run(kw, eager_first=2, replays=5)
+
+
+def test_graph_refused_before_average_starts():
+    announce("graph: capture refused before the weight average starts")
+    p = _params(8)
+    opt = mo.Muon(p, beta_ema=0.99, ema_start=3)
+    with pytest.raises(ValueError):
+        opt.graph(_grads(8, 0))
+    assert opt.step_count == 0
