@@ -104,14 +104,18 @@ double plan_cost(const std::vector<std::pair<std::pair<int, int>, int>>& shapes,
   return (phase(gram, gmax, gt) + phase(poly, pmax, pt) + phase(apply, amax, at)) / tile_eff(ts);
 }
 
-int choose_ts(const std::vector<std::pair<std::pair<int, int>, int>>& shapes) {
+// 256-wide tiles exist for bf16 operands only (fp32 operands would need
+// twice the fragment and epilogue registers); MUON_TILE forces a size.
+int choose_ts(const std::vector<std::pair<std::pair<int, int>, int>>& shapes, int xdt) {
+  const int top = xdt == MUON_BF16 ? 256 : 128;
   if (const char* e = std::getenv("MUON_TILE")) {
     const int v = std::atoi(e);
-    if (v == 64 || v == 128 || v == 256) return v;
+    if (v == 64 || v == 128 || v == 256) return std::min(v, top);
   }
-  int best = 256;
-  double bc = plan_cost(shapes, 256);
+  int best = top;
+  double bc = plan_cost(shapes, top);
   for (int ts : {128, 64}) {
+    if (ts >= top) continue;
     const double c = plan_cost(shapes, ts);
     if (c < bc * 0.999) { bc = c; best = ts; }
   }
@@ -144,12 +148,9 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   }
   std::vector<std::pair<std::pair<int, int>, int>> shapes;
   for (auto& g : p.groups) shapes.push_back({{g.m, g.n}, int(g.mats.size())});
-  p.ts = choose_ts(shapes);
-  // 256-wide bf16 tiles run eight waves (two per SIMD); MUON_WAVES=4 selects
-  // the one-wave-per-SIMD variant
-  p.waves = (p.ts == 256 && xdt == MUON_BF16) ? 8 : 4;
-  if (const char* e = std::getenv("MUON_WAVES"))
-    if (std::atoi(e) == 4) p.waves = 4;
+  p.ts = choose_ts(shapes, xdt);
+  // 256-wide (bf16) tiles run eight waves, two per SIMD; smaller tiles four
+  p.waves = p.ts == 256 ? 8 : 4;
 
   const int es = esize(xdt);
   size_t off = 0;
@@ -216,7 +217,7 @@ const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   std::vector<int64_t> key(2 * size_t(n));
   for (int i = 0; i < n; ++i) { key[2 * i] = rows[i]; key[2 * i + 1] = cols[i]; }
   const char* e = std::getenv("MUON_TILE");
-  const char* w = std::getenv("MUON_WAVES");
+  const char* w = nullptr;
   const char* o = std::getenv("MUON_GEMM_ORDER");
   const std::string tile_env = std::string(e ? e : "-") + "/" + (w ? w : "-") + "/" + (o ? o : "-");
   auto k = std::make_tuple(std::move(key), xdt, tile_env);
@@ -228,40 +229,54 @@ const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   return g_plans.emplace(std::move(k), std::move(p)).first->second;
 }
 
-// Device table uploads, cached per workspace so unchanged tables are not re-sent.
-struct Upload {
-  std::vector<uint8_t> bytes;
-  void* pinned = nullptr;
+// Host -> device uploads of the per-call tables (matrix descriptors and tile
+// prefix sums).  The workspace is caller memory that
+// may be freed and handed out again at the same address, so a table is sent on
+// every call instead of being trusted to still be there.  Each copy goes from
+// one slot of a ring of pinned staging buffers; a slot is reused only once the
+// event recorded behind its previous copy has completed, so the stream is
+// never synchronised.  Under graph capture nothing is sent: the table must
+// equal what the last uncaptured call (or muon_step_prepare) sent to that
+// address, and stays resident for the replays as long as no other call on the
+// workspace sends different tables.
+struct StageSlot {
+  void* host = nullptr;
   size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool used = false;
 };
-std::map<void*, Upload> g_uploads;
+constexpr int kStageRing = 16;
+StageSlot g_stage[kStageRing];
+int g_stage_next = 0;
+std::map<void*, std::vector<uint8_t>> g_sent;   // last content sent to each address
 
-// A stream under graph capture cannot take the upload (it synchronises and
-// copies from a reused host buffer): the table must already be resident, put
-// there by muon_step_prepare or an eager call with the same buffers.
-int upload_table(void* ws, const std::vector<uint8_t>& bytes, hipStream_t s) {
-  Upload& u = g_uploads[ws];
-  if (u.bytes == bytes) return MUON_OK;
+int upload_table(void* dst, const std::vector<uint8_t>& bytes, hipStream_t s) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MUON_E_HIP;
-  if (cs != hipStreamCaptureStatusNone) return MUON_E_CAPTURE;
-  hipError_t err;
-  if (u.pinned) {
-    // the previous copy from this buffer may still be queued
-    if ((err = hipStreamSynchronize(s)) != hipSuccess) return MUON_E_HIP;
+  if (cs != hipStreamCaptureStatusNone) {
+    auto it = g_sent.find(dst);
+    return (it != g_sent.end() && it->second == bytes) ? MUON_OK : MUON_E_CAPTURE;
   }
-  if (u.cap < bytes.size()) {
-    if (u.pinned) (void)hipHostFree(u.pinned);
-    u.pinned = nullptr;
-    u.cap = 0;
-    if ((err = hipHostMalloc(&u.pinned, bytes.size(), hipHostMallocDefault)) != hipSuccess)
-      return MUON_E_HIP;
-    u.cap = bytes.size();
+  StageSlot& sl = g_stage[g_stage_next];
+  g_stage_next = (g_stage_next + 1) % kStageRing;
+  if (sl.used && hipEventSynchronize(sl.ev) != hipSuccess) return MUON_E_HIP;
+  if (!sl.ev && hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming) != hipSuccess)
+    return MUON_E_HIP;
+  if (sl.cap < bytes.size()) {
+    if (sl.host) (void)hipHostFree(sl.host);   // its last copy has completed
+    sl.host = nullptr;
+    sl.cap = 0;
+    const size_t want = std::max<size_t>(bytes.size(), size_t(64) << 10);
+    if (hipHostMalloc(&sl.host, want, hipHostMallocDefault) != hipSuccess) return MUON_E_HIP;
+    sl.cap = want;
   }
-  std::memcpy(u.pinned, bytes.data(), bytes.size());
-  err = hipMemcpyAsync(ws, u.pinned, bytes.size(), hipMemcpyHostToDevice, s);
-  if (err != hipSuccess) { u.bytes.clear(); return MUON_E_HIP; }
-  u.bytes = bytes;
+  std::memcpy(sl.host, bytes.data(), bytes.size());
+  if (hipMemcpyAsync(dst, sl.host, bytes.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+    return MUON_E_HIP;
+  if (hipEventRecord(sl.ev, s) != hipSuccess) return MUON_E_HIP;
+  sl.used = true;
+  if (g_sent.size() > 256) g_sent.clear();
+  g_sent[dst] = bytes;
   return MUON_OK;
 }
 

@@ -100,8 +100,8 @@ hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_finish(const ElemArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,
                         hipStream_t s);
-// phase: 0 GRAM, 1 POLY, 2 APPLY; ts: tile edge (64, 128, 256); waves: 4,
-// or 8 for 256-wide bf16 tiles.
+// phase: 0 GRAM, 1 POLY, 2 APPLY; ts: tile edge (64, 128; 256 for bf16 only);
+// waves: 8 for 256-wide tiles, else 4.
 hipError_t launch_gemm(int phase, int xdt, int ts, int waves, const GemmArgs& a,
                        int64_t blocks, hipStream_t s);
 }  // namespace muon

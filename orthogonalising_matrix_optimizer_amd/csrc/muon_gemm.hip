@@ -516,8 +516,19 @@ __device__ __forceinline__ int xcd_block() {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
+// Constants of one Newton-Schulz iteration as seen by a tile.
+struct TileCoef {
+  float ca, cb, cc;   // a, b, c of the iteration
+  float cbb;          // APPLY: multiplier of the product (1, or b when B = bA)
+  float eps;
+  int first;          // first iteration: fold the norm scale s in
+};
+
+// One output tile (tP, tQ) of matrix `mat` of group G: K loop and epilogue.
+// smem holds NST * 2 * OPB bytes, red NW floats.
 template <int XDT, int MODE, int TS, int WGP, int WGQ>
-__global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
+__device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, int tQ,
+                                          const TileCoef& cf, uint8_t* smem, float* red) {
   using T = typename Ty<XDT>::T;
   constexpr int ES = Ty<XDT>::ES;
   constexpr int BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, NST = Ty<XDT>::NST;
@@ -525,12 +536,164 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   constexpr int WTP = TS / WGP, WTQ = TS / WGQ;
   constexpr int FP = WTP / 32, FQ = WTQ / 32;
   constexpr int OPB = TS * CPR * 16;  // LDS bytes per operand per stage
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * 2 * OPB];
   uint8_t* const sm0 = smem;
   uint8_t* const sm1 = smem + 2 * OPB;
   uint8_t* const sm2 = smem + (NST > 2 ? 4 : 0) * OPB;
   uint8_t* const sm3 = smem + (NST > 2 ? 6 : 2) * OPB;
+
+  const T* xin = static_cast<const T*>(G.xin) + static_cast<int64_t>(mat) * G.in_stride;
+  T* out = static_cast<T*>(G.out) + static_cast<int64_t>(mat) * G.out_stride;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wr = wave / WGQ, wc = wave % WGQ;
+
+  OpLoad la, lb;
+  int K;
+  if (MODE == GRAM || MODE == POLY) {
+    const int ld = MODE == GRAM ? G.np : G.mp;
+    K = ld;
+    const uint32_t bytes = static_cast<uint32_t>(G.mp) * ld * ES;
+    la.rs = make_desc(xin, bytes);
+    lb.rs = la.rs;
+    la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
+    la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
+    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+    plan_kc<CPR>(la, lane, wave);
+    plan_kc<CPR>(lb, lane, wave);
+  } else {
+    K = G.mp;
+    la.rs = make_desc(xin, static_cast<uint32_t>(G.mp) * G.np * ES);
+    la.ld_bytes = static_cast<uint32_t>(G.np) * ES;
+    la.origin = static_cast<uint32_t>(tP) * TS * ES;
+    plan_rm<TS, ES, NW>(la, lane, wave);
+    const T* bm = static_cast<const T*>(G.bop) + static_cast<int64_t>(mat) * G.b_stride;
+    lb.rs = make_desc(bm, static_cast<uint32_t>(G.mp) * G.mp * ES);
+    lb.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
+    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+    plan_kc<CPR>(lb, lane, wave);
+  }
+
+  float scale = 1.f;
+  if (cf.first) scale = matrix_scale<NW>(G.partials + static_cast<int64_t>(mat) * G.p_stride,
+                                           G.npartials, cf.eps, red);
+
+  f32x16_t acc[FP][FQ];
+#pragma unroll
+  for (int i = 0; i < FP; ++i)
+#pragma unroll
+    for (int j = 0; j < FQ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // 256-wide bf16 tiles fold the input term in during the K loop and store
+  // through LDS (APPLY keeps the plain epilogue when beta == 0)
+  constexpr bool kStaged = XDT == kBF16 && TS == 256;
+  const bool capt = kStaged && (MODE == POLY || (MODE == APPLY && cf.cbb != 0.f));
+  const float coef = MODE == POLY ? cf.cb / cf.cc : (capt ? cf.ca / cf.cbb : 0.f);
+
+  // the planner pads every dimension to a multiple of 128, so nk is a
+  // multiple of the stage count and each trip below runs the buffers in order
+  const int nk = K / BK;
+  if constexpr (NST == 4) {
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2);
+#pragma unroll 1
+    for (int kt = 0; kt < nk; kt += 4) {
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, acc);
+    }
+  } else {
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
+#pragma unroll 1
+    for (int kt = 0; kt < nk; kt += 2) {
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm1, acc);
+      if constexpr (kStaged && MODE != GRAM)
+        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt, sm0, lane, wr, wc, tP, tQ, coef, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+      if constexpr (kStaged && MODE != GRAM)
+        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt + 1, sm1, lane, wr, wc, tP, tQ, coef, acc);
+    }
+  }
+
+  // ---- epilogue
+  const int ld_out = MODE == APPLY ? G.np : G.mp;
+  const float alpha = MODE == GRAM ? scale * scale : 1.f;
+  const bool mirror = MODE != APPLY && tP != tQ;
+  if constexpr (kStaged) {
+    if (MODE == GRAM || capt) {
+      const float mult = MODE == GRAM ? alpha : MODE == POLY ? cf.cc : scale * cf.cbb;
+      staged_store<MODE, WGP, WGQ>(smem, reinterpret_cast<uint16_t*>(out), ld_out, tP, tQ,
+                                   mirror, mult, wave, lane, wr, wc, acc);
+      return;
+    }
+  }
+  // POLY and APPLY add a multiple of their input at the output positions:
+  // load all of this lane's input values first, so the loads overlap each
+  // other instead of each store waiting for its own load
+  constexpr int NV = MODE == GRAM ? 1 : FP * FQ * 4;
+  using V4 = typename std::conditional<XDT == kBF16, uint2, float4>::type;
+  V4 pre[NV];
+  if constexpr (MODE != GRAM) {
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) {
+        const int Q = tQ * TS + wc * WTQ + j * 32 + (lane & 31);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int P = tP * TS + wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
+          pre[(i * FQ + j) * 4 + rg] =
+              *reinterpret_cast<const V4*>(xin + static_cast<int64_t>(Q) * ld_out + P);
+        }
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < FP; ++i) {
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int Q = tQ * TS + wc * WTQ + j * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int P = tP * TS + wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][rg * 4 + e];
+        const int64_t qp = static_cast<int64_t>(Q) * ld_out + P;
+        if constexpr (MODE == GRAM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= alpha;
+        } else {
+          float xv[4];
+          unpack4(pre[(i * FQ + j) * 4 + rg], xv);
+          if constexpr (MODE == POLY) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = cf.cb * xv[e] + cf.cc * v[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = scale * (cf.ca * xv[e] + cf.cbb * v[e]);
+          }
+        }
+        st4(out + qp, v);
+        if (mirror) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st1(out + static_cast<int64_t>(P + e) * ld_out + Q, v[e]);
+        }
+      }
+    }
+  }
+}
+
+
+template <int XDT, int MODE, int TS, int WGP, int WGQ>
+__global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
+  constexpr int CPR = Ty<XDT>::CPR, NST = Ty<XDT>::NST;
+  constexpr int NW = WGP * WGQ;       // waves per block
+  constexpr int OPB = TS * CPR * 16;  // LDS bytes per operand per stage
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * 2 * OPB];
   __shared__ float red[NW];
 
   // ---- locate group, matrix and tile
@@ -590,161 +753,24 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
     tQ = bi + rem;
   }
 
-  const T* xin = static_cast<const T*>(G.xin) + static_cast<int64_t>(mat) * G.in_stride;
-  T* out = static_cast<T*>(G.out) + static_cast<int64_t>(mat) * G.out_stride;
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wr = wave / WGQ, wc = wave % WGQ;
-
-  OpLoad la, lb;
-  int K;
-  if (MODE == GRAM || MODE == POLY) {
-    const int ld = MODE == GRAM ? G.np : G.mp;
-    K = ld;
-    const uint32_t bytes = static_cast<uint32_t>(G.mp) * ld * ES;
-    la.rs = make_desc(xin, bytes);
-    lb.rs = la.rs;
-    la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
-    la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
-    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
-    plan_kc<CPR>(la, lane, wave);
-    plan_kc<CPR>(lb, lane, wave);
-  } else {
-    K = G.mp;
-    la.rs = make_desc(xin, static_cast<uint32_t>(G.mp) * G.np * ES);
-    la.ld_bytes = static_cast<uint32_t>(G.np) * ES;
-    la.origin = static_cast<uint32_t>(tP) * TS * ES;
-    plan_rm<TS, ES, NW>(la, lane, wave);
-    const T* bm = static_cast<const T*>(G.bop) + static_cast<int64_t>(mat) * G.b_stride;
-    lb.rs = make_desc(bm, static_cast<uint32_t>(G.mp) * G.mp * ES);
-    lb.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
-    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
-    plan_kc<CPR>(lb, lane, wave);
-  }
-
-  float scale = 1.f;
-  if (args.first) scale = matrix_scale<NW>(G.partials + static_cast<int64_t>(mat) * G.p_stride,
-                                           G.npartials, args.eps, red);
-
-  f32x16_t acc[FP][FQ];
-#pragma unroll
-  for (int i = 0; i < FP; ++i)
-#pragma unroll
-    for (int j = 0; j < FQ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // 256-wide bf16 tiles fold the input term in during the K loop and store
-  // through LDS (APPLY keeps the plain epilogue when beta == 0)
-  constexpr bool kStaged = XDT == kBF16 && TS == 256;
-  const bool capt = kStaged && (MODE == POLY || (MODE == APPLY && args.cbb != 0.f));
-  const float coef = MODE == POLY ? args.cb / args.cc : (capt ? args.ca / args.cbb : 0.f);
-
-  // the planner pads every dimension to a multiple of 128, so nk is a
-  // multiple of the stage count and each trip below runs the buffers in order
-  const int nk = K / BK;
-  if constexpr (NST == 4) {
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1);
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2);
-#pragma unroll 1
-    for (int kt = 0; kt < nk; kt += 4) {
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, acc);
-    }
-  } else {
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
-#pragma unroll 1
-    for (int kt = 0; kt < nk; kt += 2) {
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm1, acc);
-      if constexpr (kStaged && MODE != GRAM)
-        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt, sm0, lane, wr, wc, tP, tQ, coef, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
-      if constexpr (kStaged && MODE != GRAM)
-        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt + 1, sm1, lane, wr, wc, tP, tQ, coef, acc);
-    }
-  }
-
-  // ---- epilogue
-  const int ld_out = MODE == APPLY ? G.np : G.mp;
-  const float alpha = MODE == GRAM ? scale * scale : 1.f;
-  const bool mirror = MODE != APPLY && tP != tQ;
-  if constexpr (kStaged) {
-    if (MODE == GRAM || capt) {
-      const float mult = MODE == GRAM ? alpha : MODE == POLY ? args.cc : scale * args.cbb;
-      staged_store<MODE, WGP, WGQ>(smem, reinterpret_cast<uint16_t*>(out), ld_out, tP, tQ,
-                                   mirror, mult, wave, lane, wr, wc, acc);
-      return;
-    }
-  }
-  // POLY and APPLY add a multiple of their input at the output positions:
-  // load all of this lane's input values first, so the loads overlap each
-  // other instead of each store waiting for its own load
-  constexpr int NV = MODE == GRAM ? 1 : FP * FQ * 4;
-  using V4 = typename std::conditional<XDT == kBF16, uint2, float4>::type;
-  V4 pre[NV];
-  if constexpr (MODE != GRAM) {
-#pragma unroll
-    for (int i = 0; i < FP; ++i)
-#pragma unroll
-      for (int j = 0; j < FQ; ++j) {
-        const int Q = tQ * TS + wc * WTQ + j * 32 + (lane & 31);
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int P = tP * TS + wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
-          pre[(i * FQ + j) * 4 + rg] =
-              *reinterpret_cast<const V4*>(xin + static_cast<int64_t>(Q) * ld_out + P);
-        }
-      }
-  }
-#pragma unroll
-  for (int i = 0; i < FP; ++i) {
-#pragma unroll
-    for (int j = 0; j < FQ; ++j) {
-      const int Q = tQ * TS + wc * WTQ + j * 32 + (lane & 31);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int P = tP * TS + wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][rg * 4 + e];
-        const int64_t qp = static_cast<int64_t>(Q) * ld_out + P;
-        if constexpr (MODE == GRAM) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= alpha;
-        } else {
-          float xv[4];
-          unpack4(pre[(i * FQ + j) * 4 + rg], xv);
-          if constexpr (MODE == POLY) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = args.cb * xv[e] + args.cc * v[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = scale * (args.ca * xv[e] + args.cbb * v[e]);
-          }
-        }
-        st4(out + qp, v);
-        if (mirror) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st1(out + static_cast<int64_t>(P + e) * ld_out + Q, v[e]);
-        }
-      }
-    }
-  }
+  TileCoef cf;
+  cf.ca = args.ca; cf.cb = args.cb; cf.cc = args.cc; cf.cbb = args.cbb;
+  cf.eps = args.eps; cf.first = args.first;
+  gemm_tile<XDT, MODE, TS, WGP, WGQ>(G, mat, tP, tQ, cf, smem, red);
 }
 
 template <int XDT, int MODE>
 hipError_t launch_ts(int ts, int waves, const GemmArgs& a, int64_t blocks, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(blocks));
-  if (ts == 256 && waves == 8)
-    hipLaunchKernelGGL((k_gemm<XDT, MODE, 256, 2, 4>), grid, dim3(512), 0, s, a);
-  else if (ts == 256)
-    hipLaunchKernelGGL((k_gemm<XDT, MODE, 256, 2, 2>), grid, dim3(256), 0, s, a);
-  else if (ts == 128)
+  if constexpr (XDT == kBF16) {
+    if (ts == 256 && waves == 8) {
+      hipLaunchKernelGGL((k_gemm<XDT, MODE, 256, 2, 4>), grid, dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (ts == 128 && waves == 4)
     hipLaunchKernelGGL((k_gemm<XDT, MODE, 128, 2, 2>), grid, dim3(256), 0, s, a);
-  else if (ts == 64)
+  else if (ts == 64 && waves == 4)
     hipLaunchKernelGGL((k_gemm<XDT, MODE, 64, 2, 2>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
@@ -761,10 +787,9 @@ hipError_t launch_gemm(int phase, int xdt, int ts, int waves, const GemmArgs& a,
     if (phase == POLY) return launch_ts<kBF16, POLY>(ts, waves, a, blocks, s);
     return launch_ts<kBF16, APPLY>(ts, waves, a, blocks, s);
   }
-  // the fp32 path keeps four waves
-  if (phase == GRAM) return launch_ts<kF32, GRAM>(ts, 4, a, blocks, s);
-  if (phase == POLY) return launch_ts<kF32, POLY>(ts, 4, a, blocks, s);
-  return launch_ts<kF32, APPLY>(ts, 4, a, blocks, s);
+  if (phase == GRAM) return launch_ts<kF32, GRAM>(ts, waves, a, blocks, s);
+  if (phase == POLY) return launch_ts<kF32, POLY>(ts, waves, a, blocks, s);
+  return launch_ts<kF32, APPLY>(ts, waves, a, blocks, s);
 }
 
 }  // namespace muon

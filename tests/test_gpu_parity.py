@@ -344,3 +344,32 @@ def test_deterministic_and_resumable():
     for x, y in zip(a.ema, r.ema):
         assert torch.equal(x, y)
     assert r.step_count == 10 and r.ema_count == 10
+
+
+def test_workspace_reallocated_at_the_same_address():
+    """Free every buffer of a step and allocate the same configuration again:
+    the allocator tends to hand out the same addresses, so the per-call
+    descriptor table must be sent again rather than assumed to be resident."""
+    announce("step after freeing and reallocating identical buffers")
+    shapes = [(300, 520), (520, 300), (256, 256)]
+
+    def one_round():
+        dev = torch.device("cuda")
+        p = [gen.torch_param_matrix(r, c, 4, i, dev, dtype=torch.bfloat16)
+             for i, (r, c) in enumerate(shapes)]
+        g = [gen.torch_grad_matrix(r, c, 4, 0, i, dev, rms=1e-3, dtype=torch.bfloat16)
+             for i, (r, c) in enumerate(shapes)]
+        opt = mo.Muon(p, lr=0.02, wd=0.01, steps=5)
+        opt.step(g)
+        torch.cuda.synchronize()
+        out = [host(t) for t in p] + [host(m) for m in opt.mom]
+        del opt, p, g
+        torch.cuda.empty_cache()
+        return out
+
+    first = one_round()
+    for _ in range(2):
+        again = one_round()
+        for a, b in zip(first, again):
+            assert np.all(np.isfinite(b))
+            np.testing.assert_array_equal(a, b)
