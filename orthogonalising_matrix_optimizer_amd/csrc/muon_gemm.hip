@@ -182,9 +182,15 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Workgroup barrier without a memory fence.  Stage data arrive by LDS DMA
-// and are covered by wait_vm before it; fragments of the previous stage are
-// already in registers (consumed by its MFMAs) when a wave reaches it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// and are covered by wait_vm before it.  The wave's own LDS reads must have
+// returned before it: the compiler is free to sink the MFMAs of the previous
+// stage, and the waits for their operands, below a bare s_barrier, and a
+// wave past the barrier may then refill (or stage output into) a buffer that
+// a slower wave is still reading.  The wait sits in the same statement so
+// that nothing can separate the two.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Per-block load plan of one operand: buffer descriptor, per-lane offset
 // (fixed across stages) and the uniform byte offset of the tile's origin.

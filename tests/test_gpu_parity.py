@@ -373,3 +373,32 @@ def test_workspace_reallocated_at_the_same_address():
         for a, b in zip(first, again):
             assert np.all(np.isfinite(b))
             np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("tile,ns", [(64, "bf16"), (128, "bf16"), (256, "bf16"), (128, "f32")],
+                         indirect=["tile"])
+def test_twin_optimizers_stay_bitwise_equal(tile, ns):
+    """Several optimizers stepped in turn on identical buffers must agree bit
+    for bit after every step: the products have a fixed summation order, so
+    any difference means a kernel read LDS or memory that another wave was
+    still changing (block timing differs from launch to launch)."""
+    announce(f"twin optimizers, tile {tile}, {ns} operands")
+    shapes = [(768, 3072), (3072, 768), (768, 768), (200, 333), (333, 200), (64, 1000)]
+    dev = torch.device("cuda")
+    base = [gen.torch_param_matrix(r, c, 11, i, dev, dtype=torch.bfloat16)
+            for i, (r, c) in enumerate(shapes)]
+    twins = 6
+    params = [[p.clone() for p in base] for _ in range(twins)]
+    opts = [mo.Muon(p, lr=0.02, wd=0.1, beta=0.9, steps=5, ns_dtype=ns, diagnostics=True)
+            for p in params]
+    for t in range(8):
+        g = [gen.torch_grad_matrix(r, c, 11, t, i, dev, rms=1e-3, dtype=torch.bfloat16)
+             for i, (r, c) in enumerate(shapes)]
+        for o in opts:
+            o.step(g)
+        torch.cuda.synchronize()
+        for k in range(1, twins):
+            for i in range(len(shapes)):
+                assert torch.equal(opts[0].update[i], opts[k].update[i]), (t, k, i)
+                assert torch.equal(params[0][i], params[k][i]), (t, k, i)
+                assert torch.equal(opts[0].mom[i], opts[k].mom[i]), (t, k, i)
