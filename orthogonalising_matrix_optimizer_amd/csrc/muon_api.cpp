@@ -205,7 +205,11 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   for (int i = 0; i < n; ++i) {
     const GroupPlan& g = p.groups[p.mat_group[i]];
     p.pprefix[i + 1] = p.pprefix[i] + g.npart;
-    p.fprefix[i + 1] = p.fprefix[i] + ((rows[i] + kEw - 1) / kEw) * ((cols[i] + kEw - 1) / kEw);
+    // finish and blend: 64 x 64 tiles for tall matrices (transposed through
+    // LDS), 32 x 128 row strips otherwise
+    p.fprefix[i + 1] = p.fprefix[i] + (rows[i] > cols[i]
+        ? ((rows[i] + kEw - 1) / kEw) * ((cols[i] + kEw - 1) / kEw)
+        : ((rows[i] + kStripRows - 1) / kStripRows) * ((cols[i] + kStripCols - 1) / kStripCols));
   }
 }
 

@@ -19,6 +19,10 @@ namespace muon {
 
 constexpr int kThreads = 256;     // threads per block, every kernel
 constexpr int kEw = 64;           // edge of the elementwise (prepare/finish) tiles
+// row strips of the elementwise kernels for matrices kept in their layout;
+// a strip holds as many elements as a tile, so both give the same partial count
+constexpr int kStripRows = 32, kStripCols = 128;
+static_assert(kStripRows * kStripCols == kEw * kEw, "strip and tile sizes");
 constexpr int kMaxGroups = 8;     // effective-shape groups per grouped launch
 
 enum ElemType : int32_t { kBF16 = 0, kF32 = 1 };

@@ -125,6 +125,68 @@ __device__ __forceinline__ void storef16(float* row, bool vec, int valid, float*
   store16(row, kF32, vec, valid, v);
 }
 
+// 8 contiguous values of a row of bf16 or fp32 data (one 16-byte or two
+// 16-byte accesses when `vec`: the row start and every 8-element group are
+// 16-byte aligned).
+__device__ __forceinline__ void load8(const void* row, int dt, bool vec, int valid, float* v) {
+  if (vec && valid >= 8) {
+    if (dt == kBF16) {
+      const uint4 q = *reinterpret_cast<const uint4*>(row);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(row);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < valid)
+        v[k] = dt == kBF16 ? bf2f(static_cast<const uint16_t*>(row)[k])
+                           : static_cast<const float*>(row)[k];
+      else
+        v[k] = 0.f;
+    }
+  }
+}
+
+// Store 8 values to a row of bf16 (RNE) or fp32 data; v returns the stored values.
+__device__ __forceinline__ void store8(void* row, int dt, bool vec, int valid, float* v) {
+  if (dt == kBF16) {
+    uint16_t h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { h[k] = f2bf(v[k]); v[k] = bf2f(h[k]); }
+    if (vec && valid >= 8) {
+      uint4 q;
+      q.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+      q.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
+      q.z = static_cast<uint32_t>(h[4]) | (static_cast<uint32_t>(h[5]) << 16);
+      q.w = static_cast<uint32_t>(h[6]) | (static_cast<uint32_t>(h[7]) << 16);
+      *reinterpret_cast<uint4*>(row) = q;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < valid) static_cast<uint16_t*>(row)[k] = h[k];
+    }
+  } else {
+    if (vec && valid >= 8) {
+      float4* p = reinterpret_cast<float4*>(row);
+      p[0] = make_float4(v[0], v[1], v[2], v[3]);
+      p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < valid) static_cast<float*>(row)[k] = v[k];
+    }
+  }
+}
+
 // Matrix scale s = 1 / (sqrt(sum of partials) + eps); same order everywhere.
 __device__ __forceinline__ float matrix_scale(const float* partials, int count, float eps,
                                               float* red) {
@@ -135,6 +197,179 @@ __device__ __forceinline__ float matrix_scale(const float* partials, int count, 
 }
 
 // --------------------------------------------------------------------------
+// Row strips of 32 rows x 128 columns for matrices that keep their layout
+// (rows <= cols): thread t takes 8 consecutive elements of row t / 16 and of
+// row t / 16 + 16, so each wave access covers four whole 256-byte (bf16) or
+// 512-byte (fp32) row segments.  A strip holds as many elements as a 64 x 64
+// tile, so the strip count of the padded iterate equals its partial count.
+// Tall matrices keep 64 x 64 tiles, transposed through LDS.
+template <bool STEP, bool SLOW>
+__device__ __forceinline__ void prepare_strip(const ElemArgs& a, const MatDesc& d, int local,
+                                              float* red) {
+  const int spr = d.np / kStripCols;
+  const int si = local / spr, sj = local - si * spr;
+  const int t = threadIdx.x, lr = t >> 4;
+  const int sc = sj * kStripCols + (t & 15) * 8;
+  const int gsz = d.gdt == kBF16 ? 2 : 4;
+  int sr[2], valid[2];
+  float g[2][8], m[2][8], sl[2][8];
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    sr[ps] = si * kStripRows + lr + 16 * ps;
+    valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
+  }
+  // every load of the strip in flight before any arithmetic
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    if (valid[ps] <= 0) continue;
+    const char* grow = static_cast<const char*>(d.g) + (static_cast<int64_t>(sr[ps]) * d.ldg + sc) * gsz;
+    load8(grow, d.gdt, d.gvec, valid[ps], g[ps]);
+    if (STEP) {
+      const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+      load8(d.mom + di, kF32, d.dvec, valid[ps], m[ps]);
+      if (SLOW) load8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
+    }
+  }
+  float ss = 0.f;
+  const int xsz = a.xdt == kBF16 ? 2 : 4;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    float u[8];
+    if (valid[ps] <= 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) u[k] = 0.f;
+    } else if (STEP) {
+      const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m[ps][k] = a.beta * m[ps][k] + a.obeta * g[ps][k];
+      store8(d.mom + di, kF32, d.dvec, valid[ps], m[ps]);
+      if (SLOW) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sl[ps][k] = a.bslow * sl[ps][k] + a.obslow * g[ps][k];
+        store8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        u[k] = a.nesterov ? a.beta * m[ps][k] + a.obeta * g[ps][k] : m[ps][k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) u[k] = g[ps][k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss = ss + u[k] * u[k];
+    // X0 row sr (< mp), columns sc .. sc+7 (< np): always in bounds, padding gets zeros
+    char* xrow = static_cast<char*>(d.x0) + (static_cast<int64_t>(sr[ps]) * d.np + sc) * xsz;
+    store8(xrow, a.xdt, true, 8, u);
+  }
+  const float tot = block_sum(ss, red);
+  if (t == 0) d.partials[local] = tot;
+}
+
+template <bool STEP, bool CAUT, bool EMA>
+__device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d, int local,
+                                             float* red) {
+  const int spr = (d.cols + kStripCols - 1) / kStripCols;
+  const int si = local / spr, sj = local - si * spr;
+  const int t = threadIdx.x, lr = t >> 4;
+  const int sc = sj * kStripCols + (t & 15) * 8;
+  const int esz = a.xdt == kBF16 ? 2 : 4;
+  const int wsz = d.wdt == kBF16 ? 2 : 4;
+  const void* xb = a.final_buf ? d.x1 : d.x0;
+  int sr[2], valid[2];
+  float o[2][8], w[2][8], sl[2][8], e[2][8];
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    sr[ps] = si * kStripRows + lr + 16 * ps;
+    valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
+  }
+  constexpr bool upd = STEP;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    if (valid[ps] <= 0) continue;
+    // X rows sr < mp and columns sc .. sc+7 < np: in bounds
+    load8(static_cast<const char*>(xb) + (static_cast<int64_t>(sr[ps]) * d.np + sc) * esz, a.xdt,
+          true, 8, o[ps]);
+    if (upd) {
+      const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+      load8(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
+            d.wdt, d.wvec, valid[ps], w[ps]);
+      if (CAUT) load8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
+      if (EMA && !a.ema_first) load8(d.ema + di, kF32, d.dvec, valid[ps], e[ps]);
+    }
+  }
+  if (a.scale_o) {
+    const float s = matrix_scale(d.partials, d.npartials, a.eps, red);
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[ps][k] = s * o[ps][k];
+  }
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    if (valid[ps] <= 0) continue;
+    char* wrow = static_cast<char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz;
+    if (!upd) {                   // orthogonalize: out = O
+      store8(wrow, d.wdt, d.wvec, valid[ps], o[ps]);
+      continue;
+    }
+    const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+    float mk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      mk[k] = !CAUT || ((w[ps][k] > 0.f && sl[ps][k] > 0.f) ||
+                              (w[ps][k] < 0.f && sl[ps][k] < 0.f)) ? 1.f : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float dk = mk[k] != 0.f ? a.lrwd : 0.f;
+      w[ps][k] = (w[ps][k] - dk * w[ps][k]) - a.lr * o[ps][k];
+    }
+    store8(wrow, d.wdt, d.wvec, valid[ps], w[ps]);   // w now holds the stored values
+    if (EMA) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        e[ps][k] = a.ema_first ? w[ps][k] : a.bema * e[ps][k] + a.obema * w[ps][k];
+      store8(d.ema + di, kF32, d.dvec, valid[ps], e[ps]);
+    }
+    if (d.mask_out) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < valid[ps]) d.mask_out[di + k] = mk[k] != 0.f ? 1 : 0;
+    }
+    if (d.upd_out) store8(d.upd_out + di, kF32, d.dvec, valid[ps], o[ps]);
+  }
+}
+
+__device__ __forceinline__ void blend_strip(const ElemArgs& a, const MatDesc& d, int local,
+                                            float wf, float owf) {
+  const int spr = (d.cols + kStripCols - 1) / kStripCols;
+  const int si = local / spr, sj = local - si * spr;
+  const int t = threadIdx.x, lr = t >> 4;
+  const int sc = sj * kStripCols + (t & 15) * 8;
+  const int gsz = d.gdt == kBF16 ? 2 : 4, wsz = d.wdt == kBF16 ? 2 : 4;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    const int sr = si * kStripRows + lr + 16 * ps;
+    const int valid = sr < d.rows ? max(0, min(8, d.cols - sc)) : 0;
+    if (valid <= 0) continue;
+    float w[8], e[8];
+    load8(static_cast<const char*>(d.g) + (static_cast<int64_t>(sr) * d.ldg + sc) * gsz, d.gdt,
+          d.gvec, valid, w);
+    load8(d.ema + static_cast<int64_t>(sr) * d.cols + sc, kF32, d.dvec, valid, e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = wf * w[k] + owf * e[k];
+    store8(static_cast<char*>(d.w) + (static_cast<int64_t>(sr) * d.ldw + sc) * wsz, d.wdt,
+           d.wvec, valid, w);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Tall matrices (rows > cols): the 64 x 64 source tile at (source rows
+// tj*64.., source columns ti*64..) becomes X0 tile (ti, tj) through a padded
+// LDS tile.  Thread t reads 8 consecutive source elements of rows t / 8 and
+// t / 8 + 32 and writes 8 consecutive X0 elements of rows t / 8 and t / 8 + 32;
+// both LDS patterns touch 64 distinct banks per wave.
+// STEP: optimizer step (else orthogonalize input); SLOW: slow momentum.
+template <bool STEP, bool SLOW>
 __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
   __shared__ float tile[kEw][kEw + 1];
   __shared__ float red[4];
@@ -142,73 +377,85 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
   const int mi = find_mat(a.prefix, a.nmats, b);
   const MatDesc& d = a.mats[mi];
   const int local = static_cast<int>(b - a.prefix[mi]);
+  if (!d.tall) {
+    prepare_strip<STEP, SLOW>(a, d, local, red);
+    return;
+  }
   const int tpr = d.np / kEw;
   const int ti = local / tpr, tj = local - ti * tpr;
-  const int tall = d.tall;
-  const int sr0 = tall ? tj * kEw : ti * kEw;
-  const int sc0 = tall ? ti * kEw : tj * kEw;
-  const int t = threadIdx.x, lr = t >> 2, lc0 = (t & 3) * 16;
-  const int sr = sr0 + lr, sc = sc0 + lc0;
-  const int valid = sr < d.rows ? max(0, min(16, d.cols - sc)) : 0;
-
-  float u[16];
-  if (a.mode == 0) {
-    float g[16], m[16];
-    const int64_t gi = static_cast<int64_t>(sr) * d.ldg + sc;
-    const int64_t di = static_cast<int64_t>(sr) * d.cols + sc;
-    const char* grow = static_cast<const char*>(d.g) + gi * (d.gdt == kBF16 ? 2 : 4);
-    if (valid > 0) {
-      load16(grow, d.gdt, d.gvec, valid, g);
-      loadf16(d.mom + di, d.dvec, valid, m);
+  const int t = threadIdx.x, lr = t >> 3, lc = (t & 7) * 8;
+  const int sc = ti * kEw + lc;
+  const int gsz = d.gdt == kBF16 ? 2 : 4;
+  int sr[2], valid[2];
+  float g[2][8], m[2][8], sl[2][8];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) m[k] = a.beta * m[k] + a.obeta * g[k];
-      storef16(d.mom + di, d.dvec, valid, m);
-      if (a.use_slow) {
-        float s[16];
-        loadf16(d.slow + di, d.dvec, valid, s);
+  for (int ps = 0; ps < 2; ++ps) {
+    sr[ps] = tj * kEw + lr + 32 * ps;
+    valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
+  }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) s[k] = a.bslow * s[k] + a.obslow * g[k];
-        storef16(d.slow + di, d.dvec, valid, s);
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        u[k] = a.nesterov ? a.beta * m[k] + a.obeta * g[k] : m[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) u[k] = 0.f;
-    }
-  } else {
-    const int64_t gi = static_cast<int64_t>(sr) * d.ldg + sc;
-    const char* grow = static_cast<const char*>(d.g) + gi * (d.gdt == kBF16 ? 2 : 4);
-    if (valid > 0) {
-      load16(grow, d.gdt, d.gvec, valid, u);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) u[k] = 0.f;
+  for (int ps = 0; ps < 2; ++ps) {
+    if (valid[ps] <= 0) continue;
+    const char* grow = static_cast<const char*>(d.g) + (static_cast<int64_t>(sr[ps]) * d.ldg + sc) * gsz;
+    load8(grow, d.gdt, d.gvec, valid[ps], g[ps]);
+    if (STEP) {
+      const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+      load8(d.mom + di, kF32, d.dvec, valid[ps], m[ps]);
+      if (SLOW) load8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
     }
   }
-  // entries past the valid run are zero already; sum of squares of U
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) ss = ss + u[k] * u[k];
-
-  if (tall) {
+  for (int ps = 0; ps < 2; ++ps) {
+    float u[8];
+    if (valid[ps] <= 0) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) tile[lr][lc0 + k] = u[k];
-    __syncthreads();
+      for (int k = 0; k < 8; ++k) u[k] = 0.f;
+    } else if (STEP) {
+      const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) u[k] = tile[lc0 + k][lr];
+      for (int k = 0; k < 8; ++k) m[ps][k] = a.beta * m[ps][k] + a.obeta * g[ps][k];
+      store8(d.mom + di, kF32, d.dvec, valid[ps], m[ps]);
+      if (SLOW) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sl[ps][k] = a.bslow * sl[ps][k] + a.obslow * g[ps][k];
+        store8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        u[k] = a.nesterov ? a.beta * m[ps][k] + a.obeta * g[ps][k] : m[ps][k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) u[k] = g[ps][k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ss = ss + u[k] * u[k];
+      tile[lr + 32 * ps][lc + k] = u[k];
+    }
   }
-  // X0 row (ti*64 + lr), columns (tj*64 + lc0 ...), ld = np, always in bounds
-  const int64_t xi = static_cast<int64_t>(ti * kEw + lr) * d.np + tj * kEw + lc0;
-  char* xrow = static_cast<char*>(d.x0) + xi * (a.xdt == kBF16 ? 2 : 4);
-  store16(xrow, a.xdt, true, 16, u);
-
+  __syncthreads();
+  // X0 rows ti*64 + lr (+32) (source columns), columns tj*64 + lc .. (source
+  // rows), ld = np: always in bounds, padding gets zeros
+  const int xsz = a.xdt == kBF16 ? 2 : 4;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    float u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) u[k] = tile[lc + k][lr + 32 * ps];
+    const int64_t xi = static_cast<int64_t>(ti * kEw + lr + 32 * ps) * d.np + tj * kEw + lc;
+    store8(static_cast<char*>(d.x0) + xi * xsz, a.xdt, true, 8, u);
+  }
   const float tot = block_sum(ss, red);
   if (t == 0) d.partials[local] = tot;
 }
 
 // --------------------------------------------------------------------------
+// Tall matrices: O tile at (source rows fi*64.., source columns fj*64..) is
+// the transpose of the X tile at (rows fj*64.., columns fi*64..), staged
+// through LDS as in k_prepare.
+// STEP: optimizer update (else store O); CAUT: cautious mask; EMA: weight average.
+template <bool STEP, bool CAUT, bool EMA>
 __global__ __launch_bounds__(kThreads) void k_finish(ElemArgs a) {
   __shared__ float tile[kEw][kEw + 1];
   __shared__ float red[4];
@@ -216,79 +463,88 @@ __global__ __launch_bounds__(kThreads) void k_finish(ElemArgs a) {
   const int mi = find_mat(a.prefix, a.nmats, b);
   const MatDesc& d = a.mats[mi];
   const int local = static_cast<int>(b - a.prefix[mi]);
+  if (!d.tall) {
+    finish_strip<STEP, CAUT, EMA>(a, d, local, red);
+    return;
+  }
   const int tpr = (d.cols + kEw - 1) / kEw;
   const int fi = local / tpr, fj = local - fi * tpr;
-  const int t = threadIdx.x, lr = t >> 2, lc0 = (t & 3) * 16;
-  const int sr = fi * kEw + lr, sc = fj * kEw + lc0;
+  const int t = threadIdx.x, lr = t >> 3, lc = (t & 7) * 8;
   const int esz = a.xdt == kBF16 ? 2 : 4;
+  const int wsz = d.wdt == kBF16 ? 2 : 4;
   const void* xb = a.final_buf ? d.x1 : d.x0;
-
-  float o[16];
-  if (d.tall) {
-    // O[sr][sc] = X[sc][sr]; stage X rows (fj*64 + lr), cols (fi*64 + lc0..)
-    const int64_t xi = static_cast<int64_t>(fj * kEw + lr) * d.np + fi * kEw + lc0;
-    float v[16];
-    load16(static_cast<const char*>(xb) + xi * esz, a.xdt, true, 16, v);
+  const int sc = fj * kEw + lc;
+  int sr[2], valid[2];
+  float x[2][8], w[2][8], sl[2][8], e[2][8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) tile[lr][lc0 + k] = v[k];
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) o[k] = tile[lc0 + k][lr];
-  } else {
-    const int64_t xi = static_cast<int64_t>(sr) * d.np + sc;
-    load16(static_cast<const char*>(xb) + xi * esz, a.xdt, true, 16, o);
+  for (int ps = 0; ps < 2; ++ps) {
+    sr[ps] = fi * kEw + lr + 32 * ps;
+    valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
+    // X rows fj*64 + lr (+32) < mp, columns fi*64 + lc .. < np: in bounds
+    const int64_t xi = static_cast<int64_t>(fj * kEw + lr + 32 * ps) * d.np + fi * kEw + lc;
+    load8(static_cast<const char*>(xb) + xi * esz, a.xdt, true, 8, x[ps]);
   }
+  if (STEP) {
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      if (valid[ps] <= 0) continue;
+      const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+      load8(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
+            d.wdt, d.wvec, valid[ps], w[ps]);
+      if (CAUT) load8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
+      if (EMA && !a.ema_first) load8(d.ema + di, kF32, d.dvec, valid[ps], e[ps]);
+    }
+  }
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tile[lr + 32 * ps][lc + k] = x[ps][k];
+  __syncthreads();
+  float o[2][8];
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[ps][k] = tile[lc + k][lr + 32 * ps];
   if (a.scale_o) {
     const float s = matrix_scale(d.partials, d.npartials, a.eps, red);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o[k] = s * o[k];
-  }
-  const int valid = sr < d.rows ? max(0, min(16, d.cols - sc)) : 0;
-  if (valid <= 0) return;
-
-  const int64_t wi = static_cast<int64_t>(sr) * d.ldw + sc;
-  char* wrow = static_cast<char*>(d.w) + wi * (d.wdt == kBF16 ? 2 : 4);
-  const int64_t di = static_cast<int64_t>(sr) * d.cols + sc;
-  if (a.mode == 1) {            // orthogonalize: out = O
-    store16(wrow, d.wdt, d.wvec, valid, o);
-    return;
-  }
-  float w[16], mk[16];
-  load16(wrow, d.wdt, d.wvec, valid, w);
-  if (a.cautious) {
-    float s[16];
-    loadf16(d.slow + di, d.dvec, valid, s);
+    for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      mk[k] = ((w[k] > 0.f && s[k] > 0.f) || (w[k] < 0.f && s[k] < 0.f)) ? 1.f : 0.f;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) mk[k] = 1.f;
+      for (int k = 0; k < 8; ++k) o[ps][k] = s * o[ps][k];
   }
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float dk = mk[k] != 0.f ? a.lrwd : 0.f;
-    w[k] = (w[k] - dk * w[k]) - a.lr * o[k];
-  }
-  store16(wrow, d.wdt, d.wvec, valid, w);   // w now holds the stored values
-  if (a.ema_on) {
-    float e[16];
-    if (a.ema_first) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) e[k] = w[k];
-    } else {
-      loadf16(d.ema + di, d.dvec, valid, e);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) e[k] = a.bema * e[k] + a.obema * w[k];
+  for (int ps = 0; ps < 2; ++ps) {
+    if (valid[ps] <= 0) continue;
+    char* wrow = static_cast<char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz;
+    if (!STEP) {                  // orthogonalize: out = O
+      store8(wrow, d.wdt, d.wvec, valid[ps], o[ps]);
+      continue;
     }
-    storef16(d.ema + di, d.dvec, valid, e);
-  }
-  if (d.mask_out) {
+    const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
+    float mk[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k < valid) d.mask_out[di + k] = mk[k] != 0.f ? 1 : 0;
+    for (int k = 0; k < 8; ++k)
+      mk[k] = !CAUT || ((w[ps][k] > 0.f && sl[ps][k] > 0.f) ||
+                        (w[ps][k] < 0.f && sl[ps][k] < 0.f)) ? 1.f : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float dk = mk[k] != 0.f ? a.lrwd : 0.f;
+      w[ps][k] = (w[ps][k] - dk * w[ps][k]) - a.lr * o[ps][k];
+    }
+    store8(wrow, d.wdt, d.wvec, valid[ps], w[ps]);   // w now holds the stored values
+    if (EMA) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        e[ps][k] = a.ema_first ? w[ps][k] : a.bema * e[ps][k] + a.obema * w[ps][k];
+      store8(d.ema + di, kF32, d.dvec, valid[ps], e[ps]);
+    }
+    if (d.mask_out) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < valid[ps]) d.mask_out[di + k] = mk[k] != 0.f ? 1 : 0;
+    }
+    if (d.upd_out) store8(d.upd_out + di, kF32, d.dvec, valid[ps], o[ps]);
   }
-  if (d.upd_out) storef16(d.upd_out + di, d.dvec, valid, o);
 }
 
 // --------------------------------------------------------------------------
@@ -298,6 +554,10 @@ __global__ __launch_bounds__(kThreads) void k_blend(ElemArgs a, float wf, float 
   const int mi = find_mat(a.prefix, a.nmats, b);
   const MatDesc& d = a.mats[mi];
   const int local = static_cast<int>(b - a.prefix[mi]);
+  if (!d.tall) {
+    blend_strip(a, d, local, wf, owf);
+    return;
+  }
   const int tpr = (d.cols + kEw - 1) / kEw;
   const int fi = local / tpr, fj = local - fi * tpr;
   const int t = threadIdx.x, lr = t >> 2, lc0 = (t & 3) * 16;
@@ -318,13 +578,29 @@ __global__ __launch_bounds__(kThreads) void k_blend(ElemArgs a, float wf, float 
 
 hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prepare, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (a.mode == 1)
+    hipLaunchKernelGGL((k_prepare<false, false>), grid, dim3(kThreads), 0, s, a);
+  else if (a.use_slow)
+    hipLaunchKernelGGL((k_prepare<true, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_prepare<true, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_finish(const ElemArgs& a, int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_finish, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
+  const dim3 grid(static_cast<uint32_t>(blocks)), blk(kThreads);
+  if (a.mode == 1)
+    hipLaunchKernelGGL((k_finish<false, false, false>), grid, blk, 0, s, a);
+  else if (a.cautious && a.ema_on)
+    hipLaunchKernelGGL((k_finish<true, true, true>), grid, blk, 0, s, a);
+  else if (a.cautious)
+    hipLaunchKernelGGL((k_finish<true, true, false>), grid, blk, 0, s, a);
+  else if (a.ema_on)
+    hipLaunchKernelGGL((k_finish<true, false, true>), grid, blk, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_finish<true, false, false>), grid, blk, 0, s, a);
   return hipGetLastError();
 }
 
