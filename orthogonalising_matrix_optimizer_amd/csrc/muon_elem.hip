@@ -22,6 +22,22 @@
 namespace muon {
 namespace {
 
+// Pointers read from the descriptor table are generic to the compiler, which
+// would then use flat instructions; those also count on the LDS/scalar wait
+// counter, so every scalar load or LDS wait would drain the streaming loads
+// first.  The data are device global memory: access them through address
+// space 1.
+// (The host pass of this file only parses device code: no address spaces there.)
+#if defined(__HIP_DEVICE_COMPILE__)
+#define GAS __attribute__((address_space(1)))
+#else
+#define GAS
+#endif
+template <class T>
+__device__ __forceinline__ GAS T* glb(T* p) { return (GAS T*)(p); }
+template <class T>
+__device__ __forceinline__ const GAS T* glb(const T* p) { return (const GAS T*)(p); }
+
 __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
@@ -59,7 +75,7 @@ __device__ __forceinline__ void load16(const void* row, int dt, bool vec, int va
                                        float* v) {
   if (vec && valid >= 16) {
     if (dt == kBF16) {
-      const uint4* p = reinterpret_cast<const uint4*>(row);
+      const uint4* p = glb(reinterpret_cast<const uint4*>(row));
       uint4 q[2] = {p[0], p[1]};
       const uint32_t* w = reinterpret_cast<const uint32_t*>(q);
 #pragma unroll
@@ -68,7 +84,7 @@ __device__ __forceinline__ void load16(const void* row, int dt, bool vec, int va
         v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
       }
     } else {
-      const float4* p = reinterpret_cast<const float4*>(row);
+      const float4* p = glb(reinterpret_cast<const float4*>(row));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float4 q = p[k];
@@ -79,8 +95,8 @@ __device__ __forceinline__ void load16(const void* row, int dt, bool vec, int va
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (k < valid)
-        v[k] = dt == kBF16 ? bf2f(static_cast<const uint16_t*>(row)[k])
-                           : static_cast<const float*>(row)[k];
+        v[k] = dt == kBF16 ? bf2f(glb(static_cast<const uint16_t*>(row))[k])
+                           : glb(static_cast<const float*>(row))[k];
       else
         v[k] = 0.f;
     }
@@ -95,25 +111,25 @@ __device__ __forceinline__ void store16(void* row, int dt, bool vec, int valid,
 #pragma unroll
     for (int k = 0; k < 16; ++k) { h[k] = f2bf(v[k]); v[k] = bf2f(h[k]); }
     if (vec && valid >= 16) {
-      uint4* p = reinterpret_cast<uint4*>(row);
+      uint4* p = glb(reinterpret_cast<uint4*>(row));
       const uint4* q = reinterpret_cast<const uint4*>(h);
       p[0] = q[0];
       p[1] = q[1];
     } else {
 #pragma unroll
       for (int k = 0; k < 16; ++k)
-        if (k < valid) static_cast<uint16_t*>(row)[k] = h[k];
+        if (k < valid) glb(static_cast<uint16_t*>(row))[k] = h[k];
     }
   } else {
     if (vec && valid >= 16) {
-      float4* p = reinterpret_cast<float4*>(row);
+      float4* p = glb(reinterpret_cast<float4*>(row));
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
     } else {
 #pragma unroll
       for (int k = 0; k < 16; ++k)
-        if (k < valid) static_cast<float*>(row)[k] = v[k];
+        if (k < valid) glb(static_cast<float*>(row))[k] = v[k];
     }
   }
 }
@@ -131,7 +147,7 @@ __device__ __forceinline__ void storef16(float* row, bool vec, int valid, float*
 __device__ __forceinline__ void load8(const void* row, int dt, bool vec, int valid, float* v) {
   if (vec && valid >= 8) {
     if (dt == kBF16) {
-      const uint4 q = *reinterpret_cast<const uint4*>(row);
+      const uint4 q = *glb(reinterpret_cast<const uint4*>(row));
       const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -139,7 +155,7 @@ __device__ __forceinline__ void load8(const void* row, int dt, bool vec, int val
         v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
       }
     } else {
-      const float4* p = reinterpret_cast<const float4*>(row);
+      const float4* p = glb(reinterpret_cast<const float4*>(row));
       const float4 a = p[0], b = p[1];
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
@@ -148,8 +164,8 @@ __device__ __forceinline__ void load8(const void* row, int dt, bool vec, int val
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (k < valid)
-        v[k] = dt == kBF16 ? bf2f(static_cast<const uint16_t*>(row)[k])
-                           : static_cast<const float*>(row)[k];
+        v[k] = dt == kBF16 ? bf2f(glb(static_cast<const uint16_t*>(row))[k])
+                           : glb(static_cast<const float*>(row))[k];
       else
         v[k] = 0.f;
     }
@@ -168,21 +184,21 @@ __device__ __forceinline__ void store8(void* row, int dt, bool vec, int valid, f
       q.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
       q.z = static_cast<uint32_t>(h[4]) | (static_cast<uint32_t>(h[5]) << 16);
       q.w = static_cast<uint32_t>(h[6]) | (static_cast<uint32_t>(h[7]) << 16);
-      *reinterpret_cast<uint4*>(row) = q;
+      *glb(reinterpret_cast<uint4*>(row)) = q;
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < valid) static_cast<uint16_t*>(row)[k] = h[k];
+        if (k < valid) glb(static_cast<uint16_t*>(row))[k] = h[k];
     }
   } else {
     if (vec && valid >= 8) {
-      float4* p = reinterpret_cast<float4*>(row);
+      float4* p = glb(reinterpret_cast<float4*>(row));
       p[0] = make_float4(v[0], v[1], v[2], v[3]);
       p[1] = make_float4(v[4], v[5], v[6], v[7]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < valid) static_cast<float*>(row)[k] = v[k];
+        if (k < valid) glb(static_cast<float*>(row))[k] = v[k];
     }
   }
 }
@@ -191,7 +207,7 @@ __device__ __forceinline__ void store8(void* row, int dt, bool vec, int valid, f
 __device__ __forceinline__ float matrix_scale(const float* partials, int count, float eps,
                                               float* red) {
   float acc = 0.f;
-  for (int i = threadIdx.x; i < count; i += kThreads) acc += partials[i];
+  for (int i = threadIdx.x; i < count; i += kThreads) acc += glb(partials)[i];
   float s = block_sum(acc, red);
   return 1.0f / (sqrtf(s) + eps);
 }
@@ -262,7 +278,7 @@ __device__ __forceinline__ void prepare_strip(const ElemArgs& a, const MatDesc& 
     store8(xrow, a.xdt, true, 8, u);
   }
   const float tot = block_sum(ss, red);
-  if (t == 0) d.partials[local] = tot;
+  if (t == 0) glb(d.partials)[local] = tot;
 }
 
 template <bool STEP, bool CAUT, bool EMA>
@@ -333,7 +349,7 @@ __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d
     if (d.mask_out) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < valid[ps]) d.mask_out[di + k] = mk[k] != 0.f ? 1 : 0;
+        if (k < valid[ps]) glb(d.mask_out)[di + k] = mk[k] != 0.f ? 1 : 0;
     }
     if (d.upd_out) store8(d.upd_out + di, kF32, d.dvec, valid[ps], o[ps]);
   }
@@ -447,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
     store8(static_cast<char*>(d.x0) + xi * xsz, a.xdt, true, 8, u);
   }
   const float tot = block_sum(ss, red);
-  if (t == 0) d.partials[local] = tot;
+  if (t == 0) glb(d.partials)[local] = tot;
 }
 
 // --------------------------------------------------------------------------
@@ -541,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_finish(ElemArgs a) {
     if (d.mask_out) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < valid[ps]) d.mask_out[di + k] = mk[k] != 0.f ? 1 : 0;
+        if (k < valid[ps]) glb(d.mask_out)[di + k] = mk[k] != 0.f ? 1 : 0;
     }
     if (d.upd_out) store8(d.upd_out + di, kF32, d.dvec, valid[ps], o[ps]);
   }
