@@ -188,7 +188,8 @@ enum {
   MUON_PHASE_GRAM = 1,     /* A = X X^T                               */
   MUON_PHASE_POLY = 2,     /* B = b A + c A^2                         */
   MUON_PHASE_APPLY = 3,    /* X <- a X + B X                          */
-  MUON_PHASE_FINISH = 4    /* update, mask, EMA (or write O)          */
+  MUON_PHASE_FINISH = 4,   /* update, mask, EMA (or write O)          */
+  MUON_PHASE_ADAMW = 5     /* the AdamW kernel of muon_adamw_step     */
 };
 
 /* Record events around each of the next `capacity` launches of `phase`
@@ -207,6 +208,61 @@ int muon_probe_disarm(void);
 int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt,
                    int32_t steps, const float* coeffs, int32_t* n_groups,
                    int32_t* tiles, int32_t cap, int32_t* launches_per_step);
+
+/* ---------------------------------------------------------------------------
+ * AdamW for the parameters that are not weight matrices.  Orthogonalisation
+ * applies only to matrix-shaped layers and the pages leave every other
+ * parameter to AdamW (page "きみはNanoGPT speedrunを知っているか？",
+ * section "Muonとは"); they give no formula, so this is the textbook update
+ * with bias-corrected moments and decay decoupled from the gradient:
+ *   t  = step + 1
+ *   m <- b1*m + (1-b1)*g,   v <- b2*v + (1-b2)*(g*g)      (fp32, each product
+ *                                                         and sum rounded)
+ *   p <- p - lr*wd*p - lr * (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps)
+ * b1, b2 are the fp32 values of beta1, beta2 and (1-b) is computed in fp32,
+ * so m and v are reproducible bit for bit; the bias terms are computed on the
+ * host in double precision.  One grouped launch covers all tensors. */
+
+/* One contiguous device tensor of any shape, seen as `numel` elements. */
+typedef struct {
+  void*   ptr;     /* device pointer, aligned to its element size; may be NULL
+                      only when numel == 0                                    */
+  int64_t numel;   /* >= 0                                                    */
+  int32_t dtype;   /* MUON_BF16 or MUON_F32                                   */
+  int32_t _pad;
+} muon_vec;
+
+typedef struct {
+  float   lr;      /* finite                                                  */
+  float   beta1;   /* in [0,1)                                                */
+  float   beta2;   /* in [0,1)                                                */
+  float   eps;     /* finite, >= 0 (eps = 0 with v = 0 divides zero by zero)  */
+  float   wd;      /* finite                                                  */
+  int32_t _pad;
+} muon_adamw_hparams;
+
+/* The buffer arrays are HOST arrays of n DEVICE pointers to dense fp32
+ * buffers of numel elements (NULL allowed where numel == 0). */
+typedef struct {
+  int32_t n;
+  int32_t _pad;
+  float** m;               /* first moments                                   */
+  float** v;               /* second moments                                  */
+  void*   workspace;       /* device scratch of >= muon_adamw_workspace_bytes  */
+  size_t  workspace_bytes;
+  int64_t step;            /* completed steps (incremented per call)          */
+} muon_adamw_state;
+
+/* Workspace bytes for n tensors (the per-call descriptor table); 0 if n < 0. */
+size_t muon_adamw_workspace_bytes(int32_t n);
+
+/* One AdamW step over n tensors: params[i] updated in place (bf16 rounded to
+ * nearest even), grads[i] of the same numel (any element type).  All of
+ * params, grads, m, v and the workspace must be pairwise disjoint.  Errors as
+ * for muon_step (MUON_E_SHAPE: negative or mismatched numel; MUON_E_HPARAM:
+ * the ranges above); n == 0 only advances the counter. */
+int muon_adamw_step(const muon_vec* params, const muon_vec* grads, muon_adamw_state* st,
+                    const muon_adamw_hparams* hp, void* stream);
 
 #ifdef __cplusplus
 }

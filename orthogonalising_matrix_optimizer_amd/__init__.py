@@ -4,8 +4,8 @@
 package only marshals torch tensors to its entry points.
 """
 from . import _lib
-from .optimizer import (CUBIC, QUINTIC, Muon, StepGraph, coeff_rows, orthogonalize, plan_info,
+from .optimizer import (CUBIC, QUINTIC, AdamW, Muon, StepGraph, coeff_rows, orthogonalize, plan_info,
                         probe_arm, probe_disarm, probe_read, workspace_bytes)
 
-__all__ = ["Muon", "StepGraph", "orthogonalize", "workspace_bytes", "plan_info", "probe_arm",
+__all__ = ["Muon", "AdamW", "StepGraph", "orthogonalize", "workspace_bytes", "plan_info", "probe_arm",
            "probe_read", "probe_disarm", "coeff_rows", "CUBIC", "QUINTIC", "_lib"]

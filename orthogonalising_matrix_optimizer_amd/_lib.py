@@ -16,7 +16,7 @@ STATUS = {
     11: "MUON_E_CAPTURE",
 }
 CODES = {v: k for k, v in STATUS.items()}
-PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4}
+PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4, "adamw": 5}
 MAX_STEPS = 16
 
 
@@ -38,6 +38,21 @@ class MuonState(ctypes.Structure):
                 ("update_out", POINTER(c_void_p)),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
                 ("step", c_int64), ("ema_count", c_int64), ("opt", MuonOptions)]
+
+
+class MuonVec(ctypes.Structure):
+    _fields_ = [("ptr", c_void_p), ("numel", c_int64), ("dtype", c_int32), ("_pad", c_int32)]
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("wd", c_float), ("_pad", c_int32)]
+
+
+class AdamWState(ctypes.Structure):
+    _fields_ = [("n", c_int32), ("_pad", c_int32), ("m", POINTER(c_void_p)),
+                ("v", POINTER(c_void_p)), ("workspace", c_void_p),
+                ("workspace_bytes", c_size_t), ("step", c_int64)]
 
 
 class MuonError(RuntimeError):
@@ -85,6 +100,11 @@ def load() -> ctypes.CDLL:
     lib.muon_plan_info.argtypes = [P(MuonMat), c_int32, P(MuonOptions), c_int32, P(c_float),
                                    P(c_int32), P(c_int32), c_int32, P(c_int32)]
     lib.muon_plan_info.restype = c_int32
+    lib.muon_adamw_workspace_bytes.argtypes = [c_int32]
+    lib.muon_adamw_workspace_bytes.restype = c_size_t
+    lib.muon_adamw_step.argtypes = [P(MuonVec), P(MuonVec), P(AdamWState), P(AdamWHparams),
+                                    c_void_p]
+    lib.muon_adamw_step.restype = c_int32
     _LIB = lib
     return lib
 
@@ -120,6 +140,15 @@ def ptr_array(ptrs):
 def float_array(vals):
     vals = [float(v) for v in vals]
     return (c_float * max(1, len(vals)))(*vals)
+
+
+def vec_array(specs) -> ctypes.Array:
+    """specs: iterable of (ptr, numel, dtype)."""
+    specs = list(specs)
+    arr = (MuonVec * max(1, len(specs)))()
+    for i, (p, ne, dt) in enumerate(specs):
+        arr[i] = MuonVec(c_void_p(p) if p else None, ne, dt, 0)
+    return arr
 
 
 _ = c_uint8

@@ -769,7 +769,8 @@ int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state
 }
 
 int muon_probe_arm(int32_t phase, int32_t capacity) {
-  if (phase < 0 || phase > 4 || capacity < 1 || capacity > 65536) return MUON_E_HPARAM;
+  if (phase < 0 || phase > MUON_PHASE_ADAMW || capacity < 1 || capacity > 65536)
+    return MUON_E_HPARAM;
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto e : g_probe.ev0) (void)hipEventDestroy(e);
   for (auto e : g_probe.ev1) (void)hipEventDestroy(e);
@@ -832,6 +833,105 @@ int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt, i
     }
     *launches_per_step = l;
   }
+  return MUON_OK;
+}
+
+
+// ---------------------------------------------------------------- AdamW
+// Workspace of muon_adamw_step: descriptor table, then block prefix sums.
+size_t adamw_off_prefix(int n) { return align_up(sizeof(VecDesc) * size_t(n), kAlign); }
+size_t adamw_total(int n) { return adamw_off_prefix(n) + align_up(sizeof(int64_t) * size_t(n + 1), kAlign); }
+
+size_t muon_adamw_workspace_bytes(int32_t n) { return n < 0 ? 0 : adamw_total(n); }
+
+int muon_adamw_step(const muon_vec* params, const muon_vec* grads, muon_adamw_state* st,
+                    const muon_adamw_hparams* hp, void* stream) {
+  if (!st || !hp) return MUON_E_NULL;
+  if (st->n < 0) return MUON_E_SHAPE;
+  const float lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->wd;
+  if (!finite(lr) || !finite(wd) || !finite(eps) || eps < 0.f) return MUON_E_HPARAM;
+  if (!(b1 >= 0.f && b1 < 1.f) || !(b2 >= 0.f && b2 < 1.f)) return MUON_E_HPARAM;
+  const int n = st->n;
+  if (n == 0) {
+    st->step += 1;
+    return MUON_OK;
+  }
+  if (!params || !grads || !st->m || !st->v) return MUON_E_NULL;
+  std::vector<Range> ranges;
+  std::vector<VecDesc> desc(n);
+  std::vector<int64_t> prefix(n + 1, 0);
+  for (int i = 0; i < n; ++i) {
+    const muon_vec& P = params[i];
+    const muon_vec& G = grads[i];
+    if (P.numel < 0 || G.numel != P.numel) return MUON_E_SHAPE;
+    if ((P.dtype != MUON_BF16 && P.dtype != MUON_F32) ||
+        (G.dtype != MUON_BF16 && G.dtype != MUON_F32))
+      return MUON_E_DTYPE;
+    const int64_t ne = P.numel;
+    float* m = st->m[i];
+    float* v = st->v[i];
+    if (ne > 0) {
+      if (!P.ptr || !G.ptr || !m || !v) return MUON_E_NULL;
+      if (reinterpret_cast<uintptr_t>(P.ptr) % esize(P.dtype) ||
+          reinterpret_cast<uintptr_t>(G.ptr) % esize(G.dtype) ||
+          reinterpret_cast<uintptr_t>(m) % 4 || reinterpret_cast<uintptr_t>(v) % 4)
+        return MUON_E_ALIGN;
+      add_range(ranges, P.ptr, size_t(ne) * esize(P.dtype));
+      add_range(ranges, G.ptr, size_t(ne) * esize(G.dtype));
+      add_range(ranges, m, size_t(ne) * 4);
+      add_range(ranges, v, size_t(ne) * 4);
+    }
+    VecDesc& d = desc[i];
+    std::memset(&d, 0, sizeof(d));
+    d.p = P.ptr; d.g = G.ptr; d.m = m; d.v = v; d.n = ne;
+    d.pdt = P.dtype; d.gdt = G.dtype;
+    d.pvec = reinterpret_cast<uintptr_t>(P.ptr) % 16 == 0;
+    d.gvec = reinterpret_cast<uintptr_t>(G.ptr) % 16 == 0;
+    d.svec = reinterpret_cast<uintptr_t>(m) % 16 == 0 && reinterpret_cast<uintptr_t>(v) % 16 == 0;
+    prefix[i + 1] = prefix[i] + (ne + kAdamChunk - 1) / kAdamChunk;
+  }
+  if (prefix[n] > int64_t(INT32_MAX)) return MUON_E_SHAPE;
+  if (!st->workspace) return MUON_E_WORKSPACE;
+  const size_t need = adamw_total(n);
+  if (st->workspace_bytes < need) return MUON_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(st->workspace) % kAlign) return MUON_E_ALIGN;
+  add_range(ranges, st->workspace, need);
+  if (overlaps(ranges)) return MUON_E_ALIAS;
+
+  std::vector<uint8_t> bytes(need, 0);
+  std::memcpy(bytes.data(), desc.data(), sizeof(VecDesc) * size_t(n));
+  std::memcpy(bytes.data() + adamw_off_prefix(n), prefix.data(), sizeof(int64_t) * size_t(n + 1));
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc;
+  if ((rc = upload_table(st->workspace, bytes, s)) != MUON_OK) return rc;
+
+  // bias terms in double from the fp32 betas; (1 - b) in fp32
+  const double t = double(st->step + 1);
+  const double c1 = 1.0 - std::pow(double(b1), t);
+  const double c2 = 1.0 - std::pow(double(b2), t);
+  AdamArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.vecs = static_cast<const VecDesc*>(st->workspace);
+  a.prefix = reinterpret_cast<const int64_t*>(static_cast<char*>(st->workspace) +
+                                              adamw_off_prefix(n));
+  a.nvec = n;
+  a.b1 = b1;
+  a.b2 = b2;
+  {
+    volatile float o1 = 1.0f - b1, o2 = 1.0f - b2, lrwd = lr * wd;   // fp32 roundings
+    a.ob1 = o1;
+    a.ob2 = o2;
+    a.lrwd = lrwd;
+  }
+  a.step_size = static_cast<float>(double(lr) / c1);
+  a.rsc2 = static_cast<float>(1.0 / std::sqrt(c2));
+  a.eps = eps;
+  probe_begin(MUON_PHASE_ADAMW, s);
+  const hipError_t err = launch_adamw(a, prefix[n], s);
+  probe_end(MUON_PHASE_ADAMW, s);
+  if (err != hipSuccess) return MUON_E_HIP;
+  st->step += 1;
   return MUON_OK;
 }
 

@@ -100,6 +100,31 @@ struct GemmArgs {
 
 // Launchers (defined in the .hip sources; called by the C ABI layer).
 namespace muon {
+// AdamW over flat tensors: descriptor per tensor (resident in the workspace)
+// and kernel arguments.  Blocks take kAdamChunk consecutive elements.
+constexpr int kAdamChunk = 4096;
+struct VecDesc {
+  void* p;              // parameters (numel elements)
+  const void* g;        // gradient
+  float* m;             // first moment
+  float* v;             // second moment
+  int64_t n;            // numel
+  int32_t pdt, gdt;     // element types of p and g
+  int32_t pvec, gvec;   // 16-byte aligned p / g (vector access)
+  int32_t svec;         // 16-byte aligned m and v
+  int32_t _pad;
+};
+struct AdamArgs {
+  const VecDesc* vecs;
+  const int64_t* prefix;   // block prefix sums per tensor (n + 1 entries)
+  int32_t nvec;
+  float b1, ob1, b2, ob2;  // betas and (1 - beta), fp32
+  float step_size;         // lr / (1 - b1^t)
+  float rsc2;              // 1 / sqrt(1 - b2^t)
+  float eps, lrwd;         // eps; lr * wd
+};
+hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s);
+
 hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_finish(const ElemArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,

@@ -12,6 +12,10 @@
 //              section's displayed equation), diagnostics; or, for the
 //              orthogonalise-only entry point, a store of O.
 //   blend    : readout mix w_final*W + (1-w_final)*E (same section).
+//   adamw    : AdamW for the parameters that are not matrices (page
+//              "きみはNanoGPT speedrunを知っているか？", section "Muonとは"
+//              leaves them to AdamW; textbook update with bias-corrected
+//              moments and decoupled decay), all tensors in one launch.
 //
 // The fp32 state recurrences must be reproducible bit for bit, so this file
 // forbids contraction: every product and sum is rounded on its own.
@@ -590,6 +594,50 @@ __global__ __launch_bounds__(kThreads) void k_blend(ElemArgs a, float wf, float 
   store16(static_cast<char*>(d.w) + wi * (d.wdt == kBF16 ? 2 : 4), d.wdt, d.wvec, valid, w);
 }
 
+// --------------------------------------------------------------------------
+// AdamW.  Block b takes elements [kAdamChunk * local, +kAdamChunk) of its
+// tensor; thread t owns 8 consecutive elements in each half of the chunk, so
+// a wave access covers 512 consecutive elements.
+//   m <- b1*m + ob1*g;  v <- b2*v + ob2*(g*g);
+//   p <- (p - lrwd*p) - step_size * (m / (sqrt(v)*rsc2 + eps))
+__global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
+  const int64_t b = blockIdx.x;
+  const int vi = find_mat(a.prefix, a.nvec, b);
+  const VecDesc& d = a.vecs[vi];
+  const int64_t base = (b - a.prefix[vi]) * kAdamChunk;
+  const int t = threadIdx.x;
+  const int psz = d.pdt == kBF16 ? 2 : 4, gsz = d.gdt == kBF16 ? 2 : 4;
+  int64_t e0[2];
+  int valid[2];
+  float p[2][8], g[2][8], m[2][8], v[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    e0[h] = base + h * (kAdamChunk / 2) + t * 8;
+    valid[h] = static_cast<int>(max(int64_t(0), min(int64_t(8), d.n - e0[h])));
+    if (valid[h] <= 0) continue;
+    load8(static_cast<const char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
+    load8(static_cast<const char*>(d.g) + e0[h] * gsz, d.gdt, d.gvec, valid[h], g[h]);
+    load8(d.m + e0[h], kF32, d.svec, valid[h], m[h]);
+    load8(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (valid[h] <= 0) continue;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      m[h][k] = a.b1 * m[h][k] + a.ob1 * g[h][k];
+      const float gg = g[h][k] * g[h][k];
+      v[h][k] = a.b2 * v[h][k] + a.ob2 * gg;
+      const float den = sqrtf(v[h][k]) * a.rsc2 + a.eps;
+      const float u = m[h][k] / den;
+      p[h][k] = (p[h][k] - a.lrwd * p[h][k]) - a.step_size * u;
+    }
+    store8(static_cast<char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
+    store8(d.m + e0[h], kF32, d.svec, valid[h], m[h]);
+    store8(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s) {
@@ -625,6 +673,12 @@ hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_blend, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a,
                      wf, owf);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_adamw, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

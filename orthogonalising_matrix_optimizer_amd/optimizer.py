@@ -251,6 +251,69 @@ class StepGraph:
             self.opt.state.ema_count += 1
 
 
+def _vec(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a GPU")
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("AdamW tensors must be contiguous")
+    return (t.data_ptr() if t.numel() else 0, t.numel(), _DT[t.dtype])
+
+
+class AdamW:
+    """AdamW over a list of contiguous tensors (the parameters that are not
+    weight matrices), one grouped launch per step; see include/muon.h.
+
+    State: fp32 first and second moments per tensor and the step counter."""
+
+    def __init__(self, params: List[torch.Tensor], lr: float = 1e-3,
+                 betas: Sequence[float] = (0.9, 0.999), eps: float = 1e-8, wd: float = 0.0):
+        self.lib = _lib.load()
+        self.params = list(params)
+        dev = self.params[0].device if self.params else torch.device("cuda")
+        self.hp = _lib.AdamWHparams(float(lr), float(betas[0]), float(betas[1]), float(eps),
+                                    float(wd), 0)
+        self.m = [torch.zeros(p.numel(), dtype=torch.float32, device=dev) for p in self.params]
+        self.v = [torch.zeros(p.numel(), dtype=torch.float32, device=dev) for p in self.params]
+        n = len(self.params)
+        self.workspace = torch.empty(int(self.lib.muon_adamw_workspace_bytes(n)),
+                                     dtype=torch.uint8, device=dev)
+        self._pvecs = _lib.vec_array(_vec(p) for p in self.params)
+        self._mp = _lib.ptr_array(t.data_ptr() if t.numel() else 0 for t in self.m)
+        self._vp = _lib.ptr_array(t.data_ptr() if t.numel() else 0 for t in self.v)
+        self.state = _lib.AdamWState(n, 0, ctypes_cast(self._mp), ctypes_cast(self._vp),
+                                     self.workspace.data_ptr(), self.workspace.numel(), 0)
+        self._gkey = None
+        self._gvecs = None
+
+    @property
+    def step_count(self) -> int:
+        return int(self.state.step)
+
+    def step(self, grads: List[torch.Tensor], lr: Optional[float] = None) -> None:
+        key = tuple((g.data_ptr(), g.dtype, g.numel()) for g in grads)
+        if key != self._gkey:
+            self._gvecs = _lib.vec_array(_vec(g) for g in grads)
+            self._gkey = key
+        hp = self.hp
+        if lr is not None:
+            hp = _lib.AdamWHparams(float(lr), hp.beta1, hp.beta2, hp.eps, hp.wd, 0)
+        code = self.lib.muon_adamw_step(self._pvecs, self._gvecs, self.state, hp, _stream())
+        _lib.check(code, "muon_adamw_step")
+
+    def state_dict(self) -> Dict:
+        return {"step": self.step_count, "m": [t.clone() for t in self.m],
+                "v": [t.clone() for t in self.v]}
+
+    def load_state_dict(self, sd: Dict) -> None:
+        for dst, src in zip(self.m, sd["m"]):
+            dst.copy_(src)
+        for dst, src in zip(self.v, sd["v"]):
+            dst.copy_(src)
+        self.state.step = int(sd["step"])
+
+
 def ctypes_cast(a):
     import ctypes
     return ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))

@@ -59,6 +59,14 @@ int main(void) {
   O(muon_state, mask_out); O(muon_state, update_out); O(muon_state, workspace);
   O(muon_state, workspace_bytes); O(muon_state, step); O(muon_state, ema_count);
   O(muon_state, opt);
+  printf("muon_vec %zu\nmuon_adamw_hparams %zu\nmuon_adamw_state %zu\n", sizeof(muon_vec),
+         sizeof(muon_adamw_hparams), sizeof(muon_adamw_state));
+  O(muon_vec, ptr); O(muon_vec, numel); O(muon_vec, dtype);
+  O(muon_adamw_hparams, lr); O(muon_adamw_hparams, beta1); O(muon_adamw_hparams, beta2);
+  O(muon_adamw_hparams, eps); O(muon_adamw_hparams, wd);
+  O(muon_adamw_state, n); O(muon_adamw_state, m); O(muon_adamw_state, v);
+  O(muon_adamw_state, workspace); O(muon_adamw_state, workspace_bytes);
+  O(muon_adamw_state, step);
   return 0;
 }
 """
@@ -69,7 +77,9 @@ int main(void) {
         subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(l.split() for l in lines if l.strip())
-    ct = {"muon_mat": _lib.MuonMat, "muon_options": _lib.MuonOptions, "muon_state": _lib.MuonState}
+    ct = {"muon_mat": _lib.MuonMat, "muon_options": _lib.MuonOptions, "muon_state": _lib.MuonState,
+          "muon_vec": _lib.MuonVec, "muon_adamw_hparams": _lib.AdamWHparams,
+          "muon_adamw_state": _lib.AdamWState}
     for k, v in got.items():
         if "." in k:
             s, f = k.split(".")
@@ -289,3 +299,77 @@ def test_workspace_bytes_rejects_bad_shapes(lib):
     mats = _lib.mat_array([(0, 0, 5, 5, 0)])
     assert lib.muon_workspace_bytes(mats, 1, None, 5) == 0
     assert lib.muon_workspace_bytes(None, -1, None, 5) == 0
+
+
+# ---------------------------------------------------------------- AdamW
+def _adamw_case(n_elems=(10, 0, 4096)):
+    """Fake device addresses (never dereferenced: every case below fails
+    validation, or has n == 0)."""
+    base = 1 << 40
+    specs_p, specs_g, ms, vs = [], [], [], []
+    off = 0
+    for ne in n_elems:
+        sz = max(ne, 1) * 4
+        specs_p.append((base + off if ne else 0, ne, _lib.MUON_BF16)); off += 2 * sz + 256
+        specs_g.append((base + off if ne else 0, ne, _lib.MUON_F32)); off += 2 * sz + 256
+        ms.append(base + off if ne else 0); off += 2 * sz + 256
+        vs.append(base + off if ne else 0); off += 2 * sz + 256
+    return specs_p, specs_g, ms, vs, (base + off + 4096 + 255) // 256 * 256
+
+
+def _adamw_call(lib, specs_p, specs_g, ms, vs, ws, ws_bytes=None, hp=None, n=None):
+    P = _lib.vec_array(specs_p)
+    G = _lib.vec_array(specs_g)
+    mp, vp = _lib.ptr_array(ms), _lib.ptr_array(vs)
+    st = _lib.AdamWState(len(specs_p) if n is None else n, 0,
+                         ctypes.cast(mp, ctypes.POINTER(ctypes.c_void_p)),
+                         ctypes.cast(vp, ctypes.POINTER(ctypes.c_void_p)), ws,
+                         lib.muon_adamw_workspace_bytes(len(specs_p)) if ws_bytes is None
+                         else ws_bytes, 5)
+    hp = hp or _lib.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0)
+    code = lib.muon_adamw_step(P, G, st, hp, None)
+    return code, st
+
+
+def test_adamw_workspace_bytes(lib):
+    assert lib.muon_adamw_workspace_bytes(-1) == 0
+    assert lib.muon_adamw_workspace_bytes(0) > 0
+    assert lib.muon_adamw_workspace_bytes(100) >= 100 * 48 + 101 * 8
+
+
+def test_adamw_rejects_bad_arguments(lib):
+    E = _lib.CODES
+    p, g, m, v, ws = _adamw_case()
+    HP = _lib.AdamWHparams
+    for hp in [HP(float("nan"), 0.9, 0.999, 1e-8, 0, 0), HP(1e-3, 1.0, 0.999, 1e-8, 0, 0),
+               HP(1e-3, 0.9, -0.1, 1e-8, 0, 0), HP(1e-3, 0.9, 0.999, -1e-8, 0, 0),
+               HP(1e-3, 0.9, 0.999, 1e-8, float("inf"), 0)]:
+        code, st = _adamw_call(lib, p, g, m, v, ws, hp=hp)
+        assert code == E["MUON_E_HPARAM"] and st.step == 5
+    bad = [list(x) for x in g]
+    bad[2][1] = 4095                                            # numel mismatch
+    assert _adamw_call(lib, p, [tuple(x) for x in bad], m, v, ws)[0] == E["MUON_E_SHAPE"]
+    bad = [list(x) for x in p]
+    bad[0][2] = 7                                               # unknown dtype
+    assert _adamw_call(lib, [tuple(x) for x in bad], g, m, v, ws)[0] == E["MUON_E_DTYPE"]
+    bad = [list(x) for x in p]
+    bad[0][0] += 1                                              # odd bf16 address
+    assert _adamw_call(lib, [tuple(x) for x in bad], g, m, v, ws)[0] == E["MUON_E_ALIGN"]
+    mm = list(m)
+    mm[2] = 0                                                   # missing moment buffer
+    assert _adamw_call(lib, p, g, mm, v, ws)[0] == E["MUON_E_NULL"]
+    vv = list(v)
+    vv[0] = m[0]                                                # v aliases m
+    assert _adamw_call(lib, p, g, m, vv, ws)[0] == E["MUON_E_ALIAS"]
+    assert _adamw_call(lib, p, g, m, v, ws, ws_bytes=16)[0] == E["MUON_E_WORKSPACE"]
+    assert _adamw_call(lib, p, g, m, v, 0)[0] == E["MUON_E_WORKSPACE"]
+    assert _adamw_call(lib, p, g, m, v, ws + 64)[0] == E["MUON_E_ALIGN"]
+    assert _adamw_call(lib, p, g, m, v, p[0][0])[0] == E["MUON_E_ALIAS"]
+
+
+def test_adamw_empty_call_only_advances_the_counter(lib):
+    st = _lib.AdamWState(0, 0, None, None, None, 0, 0)
+    hp = _lib.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0)
+    for t in range(1, 4):
+        assert lib.muon_adamw_step(None, None, st, hp, None) == 0
+        assert st.step == t

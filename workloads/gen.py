@@ -225,3 +225,49 @@ def torch_param_matrix(rows: int, cols: int, seed: int, index: int, device, std:
     gtr.manual_seed((seed * 1_000_003 + PARAM_STREAM) * 1_000_003 + index)
     w = torch.randn((rows, cols), generator=gtr, device=device, dtype=torch.float32).mul_(std)
     return w if dtype is None else w.to(dtype)
+
+
+# ---------------------------------------------------------------------------
+# AdamW inputs: the parameters that are not weight matrices of the blocks.
+ADAMW_STREAM = 2 ** 21
+
+
+def gpt124m_adamw_sizes() -> List[int]:
+    """Element counts of the 124M GPT-2 parameters left to AdamW: token and
+    position embeddings, then per layer LayerNorm 1 gain and bias, Q, K, V and
+    output-projection biases, LayerNorm 2 gain and bias, MLP up and down
+    biases; then the final LayerNorm gain and bias."""
+    vocab, ctx, c, layers = 50257, 1024, 768, 12
+    sizes = [vocab * c, ctx * c]
+    for _ in range(layers):
+        sizes += [c, c, c, c, c, c, c, c, 4 * c, c]
+    return sizes + [c, c]
+
+
+def flat_param(n: int, seed: int, index: int, std: float = 0.02) -> np.ndarray:
+    """fp32 draw of std * N(0,1) from default_rng([seed, 2**21, index])."""
+    rng = np.random.default_rng([seed, ADAMW_STREAM, index])
+    return (std * rng.standard_normal(n)).astype(np.float32)
+
+
+def flat_grad(n: int, seed: int, step: int, index: int, rms: float = 1e-3) -> np.ndarray:
+    """fp32 gradient draw rms * N(0,1) from default_rng([seed, 2**21 + 1 + step, index])."""
+    rng = np.random.default_rng([seed, ADAMW_STREAM + 1 + step, index])
+    return (rms * rng.standard_normal(n)).astype(np.float32)
+
+
+def flat_moments(n: int, seed: int, index: int, rms: float = 1e-3):
+    """A non-trivial AdamW state: m ~ rms*N(0,1), v = (rms*N(0,1))^2, both fp32."""
+    rng = np.random.default_rng([seed, ADAMW_STREAM - 1, index])
+    m = (rms * rng.standard_normal(n)).astype(np.float32)
+    v = np.square(rms * rng.standard_normal(n)).astype(np.float32)
+    return m, v
+
+
+def torch_flat(x: np.ndarray, device, dtype):
+    """fp32 host array -> device tensor of `dtype` (bf16 rounded to nearest even)."""
+    import torch
+    if dtype == torch.bfloat16:
+        bits = bf16_bits_from_f32(x).view(np.int16)
+        return torch.from_numpy(bits.copy()).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
