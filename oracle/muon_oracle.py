@@ -23,6 +23,10 @@ What it computes, with the passages it follows:
   * EMA weight average theta_bar_t = beta*theta_bar_{t-1} + (1-beta)*theta_t
     (same section, its displayed equation) and the final readout blend of
     35 % final weights and 65 % average (same section, paragraph after it).
+  * Weighted running mean of the weights as an alternative average: stochastic
+    weight averaging (equal weights) and weighted checkpoint averaging, both
+    named in the results table of the Slowrun page without a formula; read as
+    E_n = sum_k w_k W_k / sum_k w_k, kept as E <- (S/(S+w)) E + (w/(S+w)) W.
 
 Precision: the orthogonalisation and the parameter update are computed in
 float64.  The stored optimizer state (momentum, slow momentum, EMA) is fp32
@@ -134,6 +138,23 @@ def ema_f32(prev: np.ndarray, new: np.ndarray, beta: float) -> np.ndarray:
     return (b * p).astype(F32) + (ob * n).astype(F32)
 
 
+def running_mean_coeffs(weight_sum: float, w: float):
+    """Weighted running mean E <- b*E + ob*W with b = S/(S+w), ob = w/(S+w),
+    computed in double and rounded to fp32 (S: weights averaged so far).
+    Equal weights give the running arithmetic mean (stochastic weight
+    averaging); the Slowrun page's results table names both it and weighted
+    checkpoint averaging without giving a formula."""
+    tot = float(weight_sum) + float(w)
+    return F32(float(weight_sum) / tot), F32(float(w) / tot)
+
+
+def average_f32(prev: np.ndarray, new: np.ndarray, b, ob) -> np.ndarray:
+    """fl(fl(b*prev) + fl(ob*new)) in fp32 with given fp32 coefficients."""
+    p = np.asarray(prev, dtype=F32)
+    n = np.asarray(new, dtype=F32)
+    return ((F32(b) * p).astype(F32) + (F32(ob) * n).astype(F32)).astype(F32)
+
+
 def momentum_f32(M: np.ndarray, G: np.ndarray, beta: float) -> np.ndarray:
     """Momentum as a moving average of the gradient, fp32 operation order."""
     return ema_f32(M, G, beta)
@@ -196,7 +217,7 @@ class OracleState:
     """Optimizer state: fp32 buffers per matrix plus integer counters."""
 
     def __init__(self, shapes: Sequence, beta_slow: float = -1.0,
-                 beta_ema: float = -1.0, ema_start: int = 1):
+                 beta_ema: float = -1.0, ema_start: int = 1, avg_mode: str = "ema"):
         self.mom = [np.zeros(s, dtype=F32) for s in shapes]
         self.slow = [np.zeros(s, dtype=F32) for s in shapes] if beta_slow >= 0 else None
         self.ema = [np.zeros(s, dtype=F32) for s in shapes] if beta_ema >= 0 else None
@@ -205,12 +226,15 @@ class OracleState:
         self.ema_start = ema_start
         self.step = 0
         self.ema_count = 0
+        self.avg_mode = avg_mode      # "ema" or "weighted"
+        self.avg_sum = 0.0            # weights averaged so far ("weighted")
 
 
 def muon_step(params: List[np.ndarray], grads: List[np.ndarray], st: OracleState,
               coeffs: np.ndarray, lr: float, wd: float, beta: float,
               param_dtype: str = "bf16", eps: float = 1e-7, nesterov: bool = False,
-              cautious: bool = False, keep: bool = True) -> Dict[str, list]:
+              cautious: bool = False, keep: bool = True,
+              avg_weight: float = 1.0) -> Dict[str, list]:
     """One optimizer step over a list of matrices.
 
     params: stored parameter values (float64 arrays holding bf16/fp32 values);
@@ -221,6 +245,10 @@ def muon_step(params: List[np.ndarray], grads: List[np.ndarray], st: OracleState
     st.step += 1
     ema_on = st.ema is not None and st.step >= st.ema_start
     first_ema = ema_on and st.ema_count == 0
+    weighted = ema_on and st.avg_mode == "weighted"
+    if weighted:
+        s0 = 0.0 if first_ema else st.avg_sum
+        avg_b, avg_ob = running_mean_coeffs(s0, avg_weight)
     new_params, outs, masks = [], [], []
     for i, (W, G) in enumerate(zip(params, grads)):
         G32 = np.asarray(G, dtype=F32)
@@ -232,13 +260,20 @@ def muon_step(params: List[np.ndarray], grads: List[np.ndarray], st: OracleState
         mask = cautious_mask(W, st.slow[i]) if cautious else None
         Wn = store(update_f64(W, O, lr, wd, mask), param_dtype)
         if ema_on:
-            st.ema[i] = Wn.astype(F32) if first_ema else ema_f32(st.ema[i], Wn, st.beta_ema)
+            if first_ema:
+                st.ema[i] = Wn.astype(F32)
+            elif weighted:
+                st.ema[i] = average_f32(st.ema[i], Wn, avg_b, avg_ob)
+            else:
+                st.ema[i] = ema_f32(st.ema[i], Wn, st.beta_ema)
         new_params.append(Wn)
         if keep:
             outs.append(O)
             masks.append(mask)
     if ema_on:
         st.ema_count += 1
+    if weighted:
+        st.avg_sum = s0 + avg_weight
     return {"params": new_params, "O": outs, "mask": masks}
 
 

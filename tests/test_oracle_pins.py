@@ -381,3 +381,64 @@ def test_mask_uses_slow_not_fast_momentum():
                         cautious=True)
     assert np.all(st.mom[0] < 0) and np.all(st.slow[0] > 0)
     assert out["mask"][0].all()
+
+
+# ---------------------------------------------------------------- weighted averages
+def _averaged(ws, weights):
+    """Run the oracle's running-mean recurrence over a sequence of fp32 arrays."""
+    e, s = None, 0.0
+    for w, wt in zip(ws, weights):
+        if e is None:
+            e, s = np.asarray(w, np.float32).copy(), float(wt)
+            continue
+        b, ob = orc.running_mean_coeffs(s, wt)
+        e = orc.average_f32(e, w, b, ob)
+        s += wt
+    return e
+
+
+def test_equal_weights_give_the_arithmetic_mean():
+    """Stochastic weight averaging: the running form must reproduce the plain
+    mean of the averaged weights (up to fp32 rounding per step)."""
+    rng = np.random.default_rng(21)
+    ws = [rng.normal(0, 0.02, 500).astype(np.float32) for _ in range(9)]
+    e = _averaged(ws, [1.0] * 9)
+    ref = np.mean(np.array(ws, dtype=np.float64), axis=0)
+    np.testing.assert_allclose(e, ref, rtol=0, atol=9 * 2.0 ** -23 * 0.1)
+
+
+def test_weights_give_the_weighted_mean():
+    rng = np.random.default_rng(22)
+    wts = [0.5, 2.0, 1.0, 3.0, 0.25, 4.0]
+    ws = [rng.normal(0, 1, 300).astype(np.float32) for _ in wts]
+    e = _averaged(ws, wts)
+    ref = np.tensordot(np.array(wts), np.array(ws, dtype=np.float64), axes=1) / sum(wts)
+    np.testing.assert_allclose(e, ref, rtol=0, atol=len(wts) * 2.0 ** -22 * 4)
+    # a weighted mean differs from the plain mean here: the weights matter
+    assert np.max(np.abs(ref - np.mean(np.array(ws, np.float64), axis=0))) > 0.1
+
+
+def test_zero_weight_leaves_the_average_unchanged():
+    rng = np.random.default_rng(23)
+    a, b = (rng.normal(0, 1, 64).astype(np.float32) for _ in range(2))
+    e = _averaged([a, b], [1.0, 0.0])
+    np.testing.assert_array_equal(e, a)
+
+
+def test_oracle_step_wires_the_weighted_average():
+    """Through muon_step: with steps whose parameters are known, the state's
+    average equals the weighted mean of the stored parameters."""
+    rng = np.random.default_rng(24)
+    shape = (16, 24)
+    st = orc.OracleState([shape], beta_ema=0.0, ema_start=2, avg_mode="weighted")
+    W = orc.store(rng.normal(0, 0.02, shape), "bf16")
+    coeffs = np.repeat(np.array([gen.QUINTIC]), 5, axis=0)
+    hist, wts = [], [0.0, 1.0, 3.0, 0.5]   # the first step is outside the window
+    for t, wt in enumerate(wts):
+        G = rng.normal(0, 1e-3, shape).astype(np.float32)
+        W = orc.muon_step([W], [G], st, coeffs, 0.02, 0.1, 0.9, avg_weight=wt)["params"][0]
+        if t >= 1:
+            hist.append(W)
+    ref = np.tensordot(np.array(wts[1:]), np.array(hist), axes=1) / sum(wts[1:])
+    np.testing.assert_allclose(st.ema[0], ref, rtol=0, atol=4 * 2.0 ** -23 * 0.1)
+    assert st.ema_count == 3 and st.avg_sum == sum(wts[1:])
