@@ -129,6 +129,37 @@ def single_matrix_times(gen, mo, dev, reps):
             "graph_ms_per_step": time_graph(opt, gr, max(reps, 20))}
 
 
+def adamw_times(gen, mo, dev, reps):
+    """AdamW over the 124M model's non-matrix parameters (embeddings, LayerNorm
+    and bias vectors: 124 bf16 tensors, 39.5M elements), one grouped launch:
+    kernel time from HIP events around the launch, and whole-call time."""
+    import torch
+    sizes = gen.gpt124m_adamw_sizes()
+    params = [gen.torch_flat(gen.flat_param(n, 0, i), dev, torch.bfloat16)
+              for i, n in enumerate(sizes)]
+    grads = [gen.torch_flat(gen.flat_grad(n, 0, 0, i), dev, torch.bfloat16)
+             for i, n in enumerate(sizes)]
+    opt = mo.AdamW(params, lr=3e-3, betas=(0.9, 0.95), eps=1e-8, wd=0.0)
+    for _ in range(3):
+        opt.step(grads)
+    call_ms = _events_ms(lambda: opt.step(grads), reps)
+    mo.probe_arm("adamw", reps)
+    for _ in range(reps):
+        opt.step(grads)
+    torch.cuda.synchronize()
+    k = mo.probe_read(reps)
+    mo.probe_disarm()
+    kernel_ms = float(np.mean(k))
+    n = int(sum(sizes))
+    nbytes = n * (2 * 2 + 2 + 16)   # p bf16 read+write, g bf16, m and v fp32 read+write
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    return {"workload": "gpt124m non-matrix parameters: 124 bf16 tensors (embeddings, "
+                        "LayerNorm gains/biases, linear biases), fp32 moments",
+            "elements": n, "tensors": len(sizes), "kernel_ms": round(kernel_ms, 4),
+            "call_ms": round(call_ms, 4), "bytes_per_element": 22,
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +246,7 @@ def main():
     # launch latency dominates
     graph_ms = time_graph(opt, grads, args.steps)
     c1 = single_matrix_times(gen, mo, dev, args.steps)
+    adamw = adamw_times(gen, mo, dev, max(args.steps, 20))
 
     sym, dense = gen.ns_flops(shapes, ms.steps)
     a_flops = apply_flops(shapes)
@@ -257,6 +289,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "graph_ms_per_step": graph_ms,
         "single_matrix": c1,
+        "adamw": adamw,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, grads_bits, params_bits, coeffs, ms.lr,

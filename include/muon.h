@@ -88,7 +88,25 @@ typedef struct {
                          (needs beta_slow >= 0)                                */
   int32_t ns_dtype;   /* MUON_BF16: bf16 MFMA operands with fp32 accumulation;
                          MUON_F32: fp32 operands and accumulation              */
+  int32_t avg_mode;   /* weight average (when beta_ema >= 0): MUON_AVG_EMA, or
+                         MUON_AVG_WEIGHTED (running weighted mean, see below)  */
+  int32_t _pad;
 } muon_options;
+
+/* Weight-average recurrences E <- b*E + ob*W, E <- W at the first averaged step:
+ *   MUON_AVG_EMA:      b = beta_ema, ob = 1 - b (fp32), the exponential moving
+ *                      average of page "Training NanoGPT in 39.9 Seconds",
+ *                      section "ANVIL II와 가중치 평균";
+ *   MUON_AVG_WEIGHTED: with this step's weight w = st->avg_weight and the sum
+ *                      S of the weights averaged so far (st->avg_weight_sum),
+ *                      b = S/(S+w), ob = w/(S+w) (computed in double, rounded
+ *                      to fp32), so E is the weighted mean of the averaged
+ *                      weights: equal weights give stochastic weight averaging,
+ *                      other weights weighted checkpoint averaging (both named
+ *                      among the tricks of the Slowrun page's results table).
+ * Components whose averages follow their own schedules (the readout, matrix
+ * banks and value embeddings of the same section) use one state each. */
+enum { MUON_AVG_EMA = 0, MUON_AVG_WEIGHTED = 1 };
 
 /* Optimizer state.  The buffer arrays are HOST arrays of n DEVICE pointers;
  * every buffer is fp32, dense row-major rows x cols of the matching param. */
@@ -109,6 +127,11 @@ typedef struct {
   int64_t   step;         /* number of completed steps (incremented per call)  */
   int64_t   ema_count;    /* number of steps folded into the weight average    */
   muon_options opt;
+  float     avg_weight;   /* MUON_AVG_WEIGHTED: weight of the next averaged step
+                             (finite, >= 0; the first averaged step needs > 0) */
+  int32_t   _pad2;
+  double    avg_weight_sum; /* MUON_AVG_WEIGHTED: sum of the weights averaged so
+                             far (advanced with ema_count)                     */
 } muon_state;
 
 /* Plain-Muon defaults: no slow momentum, no EMA, eps 1e-7, ema_start 1,
@@ -128,8 +151,8 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n,
  *   U  = M, or beta*M + (1-beta)*G with Nesterov
  *   O  = orthogonalise(U) with `steps` rows of coeffs (a_j, b_j, c_j)
  *   W <- W - lr*wd*mask*W - lr*O   (mask = 1, or [W*S > 0] when cautious)
- *   step += 1;  if EMA enabled and step >= ema_start:
- *       E <- W (first averaged step) or beta_ema*E + (1-beta_ema)*W;
+ *   step += 1;  if the average is enabled and step >= ema_start:
+ *       E <- W (first averaged step) or b*E + ob*W (see MUON_AVG_*);
  *       ema_count += 1
  * params: n matrices, updated in place (bf16 is rounded to nearest even).
  * grads:  n matrices with the same shapes (any element type).

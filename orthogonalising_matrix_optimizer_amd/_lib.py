@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmuon_mi355x.so")
 
 MUON_BF16, MUON_F32 = 0, 1
+MUON_AVG_EMA, MUON_AVG_WEIGHTED = 0, 1
 STATUS = {
     0: "MUON_OK", 1: "MUON_E_NULL", 2: "MUON_E_SHAPE", 3: "MUON_E_DTYPE",
     4: "MUON_E_COEFFS", 5: "MUON_E_HPARAM", 6: "MUON_E_WORKSPACE",
@@ -28,7 +29,7 @@ class MuonMat(ctypes.Structure):
 class MuonOptions(ctypes.Structure):
     _fields_ = [("beta_slow", c_float), ("beta_ema", c_float), ("eps", c_float),
                 ("nesterov", c_int32), ("ema_start", c_int64), ("cautious", c_int32),
-                ("ns_dtype", c_int32)]
+                ("ns_dtype", c_int32), ("avg_mode", c_int32), ("_pad", c_int32)]
 
 
 class MuonState(ctypes.Structure):
@@ -37,7 +38,8 @@ class MuonState(ctypes.Structure):
                 ("ema", POINTER(c_void_p)), ("mask_out", POINTER(c_void_p)),
                 ("update_out", POINTER(c_void_p)),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-                ("step", c_int64), ("ema_count", c_int64), ("opt", MuonOptions)]
+                ("step", c_int64), ("ema_count", c_int64), ("opt", MuonOptions),
+                ("avg_weight", c_float), ("_pad2", c_int32), ("avg_weight_sum", ctypes.c_double)]
 
 
 class MuonVec(ctypes.Structure):

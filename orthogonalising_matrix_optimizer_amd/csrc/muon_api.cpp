@@ -342,6 +342,7 @@ int check_opt(const muon_options& o) {
   if (o.cautious && o.beta_slow < 0.f) return MUON_E_HPARAM;
   if (o.nesterov != 0 && o.nesterov != 1) return MUON_E_HPARAM;
   if (o.cautious != 0 && o.cautious != 1) return MUON_E_HPARAM;
+  if (o.avg_mode != MUON_AVG_EMA && o.avg_mode != MUON_AVG_WEIGHTED) return MUON_E_HPARAM;
   return MUON_OK;
 }
 
@@ -464,6 +465,7 @@ void muon_default_options(muon_options* o) {
   o->nesterov = 0;
   o->cautious = 0;
   o->ns_dtype = MUON_BF16;
+  o->avg_mode = MUON_AVG_EMA;
 }
 
 const char* muon_status_str(int s) {
@@ -515,10 +517,24 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   const muon_options& o = st->opt;
   if ((rc = check_opt(o)) != MUON_OK) return rc;
   const bool ema_on = o.beta_ema >= 0.f && st->step + 1 >= o.ema_start;
+  // weighted running mean: b = S/(S+w), ob = w/(S+w) in double, then fp32
+  const bool weighted = ema_on && o.avg_mode == MUON_AVG_WEIGHTED;
+  double avg_sum = st->avg_weight_sum;
+  float avg_b = 0.f, avg_ob = 0.f;
+  if (weighted) {
+    const double w = st->avg_weight;
+    const double s0 = st->ema_count == 0 ? 0.0 : st->avg_weight_sum;
+    if (!std::isfinite(w) || w < 0.0 || !std::isfinite(s0) || s0 < 0.0 || !(s0 + w > 0.0))
+      return MUON_E_HPARAM;
+    avg_sum = s0 + w;
+    avg_b = static_cast<float>(s0 / avg_sum);
+    avg_ob = static_cast<float>(w / avg_sum);
+  }
   if (n == 0) {
     if (prepare_only) return MUON_OK;
     st->step += 1;
     if (ema_on) st->ema_count += 1;
+    if (weighted) st->avg_weight_sum = avg_sum;
     return MUON_OK;
   }
   if (!params || !grads || !st->mom) return MUON_E_NULL;
@@ -593,7 +609,13 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   ea.beta = beta;
   ea.obeta = 1.0f - beta;
   if (o.beta_slow >= 0.f) { ea.bslow = o.beta_slow; ea.obslow = 1.0f - o.beta_slow; }
-  if (o.beta_ema >= 0.f) { ea.bema = o.beta_ema; ea.obema = 1.0f - o.beta_ema; }
+  if (weighted) {
+    ea.bema = avg_b;
+    ea.obema = avg_ob;
+  } else if (o.beta_ema >= 0.f) {
+    ea.bema = o.beta_ema;
+    ea.obema = 1.0f - o.beta_ema;
+  }
   ea.lr = lr;
   {
     volatile float lrwd = lr * wd;   // one fp32 rounding
@@ -622,6 +644,7 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   if (err != hipSuccess) return MUON_E_HIP;
   st->step += 1;
   if (ema_on) st->ema_count += 1;
+  if (weighted) st->avg_weight_sum = avg_sum;
   return MUON_OK;
 }
 }  // namespace

@@ -94,7 +94,8 @@ class Muon:
                  coeffs: Union[str, Sequence] = "quintic",
                  beta_slow: Optional[float] = None, beta_ema: Optional[float] = None,
                  ema_start: int = 1, cautious: bool = False, nesterov: bool = False,
-                 ns_dtype: str = "bf16", eps: float = 1e-7, diagnostics: bool = False):
+                 ns_dtype: str = "bf16", eps: float = 1e-7, diagnostics: bool = False,
+                 avg: str = "ema"):
         self.lib = _lib.load()
         self.params = list(params)
         self.lr, self.wd, self.beta, self.steps = float(lr), float(wd), float(beta), int(steps)
@@ -116,12 +117,14 @@ class Muon:
         self.opt.cautious = int(bool(cautious))
         self.opt.nesterov = int(bool(nesterov))
         self.opt.ns_dtype = _NSDT[ns_dtype]
+        self.opt.avg_mode = {"ema": _lib.MUON_AVG_EMA, "weighted": _lib.MUON_AVG_WEIGHTED}[avg]
         self._pmats = _lib.mat_array(_mat(p) for p in self.params)
         need = int(self.lib.muon_workspace_bytes(self._pmats, len(self.params), self.opt,
                                                  self.steps))
         self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         self.state = _lib.MuonState()
         self.state.n = len(self.params)
+        self.state.avg_weight = 1.0
         self._keep = []
         self._bind_state()
         self._gkey = None
@@ -155,6 +158,15 @@ class Muon:
     @property
     def ema_count(self) -> int:
         return int(self.state.ema_count)
+
+    @property
+    def avg_weight(self) -> float:
+        """Weight of the next averaged step (avg="weighted"; 1 = plain SWA)."""
+        return float(self.state.avg_weight)
+
+    @avg_weight.setter
+    def avg_weight(self, w: float) -> None:
+        self.state.avg_weight = float(w)
 
     def _grad_mats(self, grads: List[torch.Tensor]):
         key = tuple((g.data_ptr(), g.stride(0), g.dtype) for g in grads)
@@ -192,6 +204,7 @@ class Muon:
     def state_dict(self) -> Dict:
         return {
             "step": self.step_count, "ema_count": self.ema_count,
+            "avg_weight_sum": float(self.state.avg_weight_sum),
             "mom": [m.clone() for m in self.mom],
             "mom_slow": None if self.mom_slow is None else [m.clone() for m in self.mom_slow],
             "ema": None if self.ema is None else [m.clone() for m in self.ema],
@@ -208,6 +221,7 @@ class Muon:
                 dst.copy_(src)
         self.state.step = int(sd["step"])
         self.state.ema_count = int(sd["ema_count"])
+        self.state.avg_weight_sum = float(sd.get("avg_weight_sum", 0.0))
 
 
 class StepGraph:
@@ -225,6 +239,9 @@ class StepGraph:
     def __init__(self, opt: Muon, grads: List[torch.Tensor], lr: Optional[float] = None,
                  wd: Optional[float] = None):
         st, o = opt.state, opt.opt
+        if o.beta_ema >= 0.0 and o.avg_mode == _lib.MUON_AVG_WEIGHTED:
+            raise ValueError("the weighted average changes its coefficients every step; "
+                             "a replay would repeat the captured ones")
         if o.beta_ema >= 0.0:
             if st.step + 1 < o.ema_start or st.ema_count == 0:
                 raise ValueError("capture after the weight average has started "

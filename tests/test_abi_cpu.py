@@ -54,11 +54,11 @@ int main(void) {
   O(muon_mat, ptr); O(muon_mat, rows); O(muon_mat, cols); O(muon_mat, ld); O(muon_mat, dtype);
   O(muon_options, beta_slow); O(muon_options, beta_ema); O(muon_options, eps);
   O(muon_options, nesterov); O(muon_options, ema_start); O(muon_options, cautious);
-  O(muon_options, ns_dtype);
+  O(muon_options, ns_dtype); O(muon_options, avg_mode);
   O(muon_state, n); O(muon_state, mom); O(muon_state, mom_slow); O(muon_state, ema);
   O(muon_state, mask_out); O(muon_state, update_out); O(muon_state, workspace);
   O(muon_state, workspace_bytes); O(muon_state, step); O(muon_state, ema_count);
-  O(muon_state, opt);
+  O(muon_state, opt); O(muon_state, avg_weight); O(muon_state, avg_weight_sum);
   printf("muon_vec %zu\nmuon_adamw_hparams %zu\nmuon_adamw_state %zu\n", sizeof(muon_vec),
          sizeof(muon_adamw_hparams), sizeof(muon_adamw_state));
   O(muon_vec, ptr); O(muon_vec, numel); O(muon_vec, dtype);
@@ -373,3 +373,28 @@ def test_adamw_empty_call_only_advances_the_counter(lib):
     for t in range(1, 4):
         assert lib.muon_adamw_step(None, None, st, hp, None) == 0
         assert st.step == t
+
+
+def test_weighted_average_validation(lib):
+    """Weights of the weighted running mean: negative, non-finite, or a zero
+    first weight are rejected before any device work; with n == 0 the weight
+    sum still advances with the average's step count."""
+    E = _lib.CODES
+    st = _lib.MuonState()
+    st.n = 0
+    st.opt = _lib.default_options()
+    st.opt.beta_ema = 0.0
+    st.opt.avg_mode = _lib.MUON_AVG_WEIGHTED
+    for bad in (-1.0, float("nan"), float("inf"), 0.0):
+        st.avg_weight = bad
+        assert lib.muon_step(None, None, st, _coeffs(), 5, 0.02, 0.0, 0.95, None) == \
+            E["MUON_E_HPARAM"]
+        assert st.step == 0 and st.ema_count == 0
+    for t, w in enumerate([2.0, 0.0, 0.5], start=1):
+        st.avg_weight = w
+        assert lib.muon_step(None, None, st, _coeffs(), 5, 0.02, 0.0, 0.95, None) == 0
+        assert st.step == t and st.ema_count == t
+    assert st.avg_weight_sum == 2.5
+    st.opt.avg_mode = 7
+    assert lib.muon_step(None, None, st, _coeffs(), 5, 0.02, 0.0, 0.95, None) == \
+        E["MUON_E_HPARAM"]

@@ -243,6 +243,40 @@ def test_anvil_ten_steps_state_forced():
         assert opt.step_count == t and opt.ema_count == t
 
 
+def test_weighted_average_state_forced():
+    """Weighted running mean of the weights (SWA with unit weights, weighted
+    checkpoint averaging otherwise) from step 2 on, weights changing per step:
+    the average must equal the oracle's recurrence on the GPU's own weights,
+    bit for bit, and the weight sum must follow."""
+    announce("weighted average 6 steps")
+    shapes = [(128, 256), (256, 128), (100, 37)]
+    _, ws = _make(shapes, "bf16")
+    params = [_dev(w) for w in ws]
+    opt = mo.Muon(params, lr=0.02, wd=0.1, beta=0.9, steps=5, coeffs="quintic",
+                  beta_ema=0.0, ema_start=2, avg="weighted")
+    weights = [9.0, 1.0, 2.0, 0.5, 3.0, 1.0]    # the first is outside the window
+    E = [None] * len(shapes)
+    s = 0.0
+    for t, wt in enumerate(weights, start=1):
+        gs = [gen.bf16_bits_from_f32(gen.grad_matrix(r, c, 0, t, i, 1e-3).astype(np.float32))
+              for i, (r, c) in enumerate(shapes)]
+        opt.avg_weight = wt
+        opt.step([_dev(g) for g in gs])
+        torch.cuda.synchronize()
+        if t < 2:
+            assert opt.ema_count == 0
+            continue
+        b, ob = orc.running_mean_coeffs(s, wt)
+        for i in range(len(shapes)):
+            Wn = host(params[i])
+            E[i] = Wn.copy() if t == 2 else orc.average_f32(E[i], Wn, b, ob)
+            np.testing.assert_array_equal(host(opt.ema[i]), E[i], err_msg=f"step {t}")
+        s += wt
+        assert opt.ema_count == t - 1 and opt.state.avg_weight_sum == s
+    with pytest.raises(ValueError):
+        opt.graph([_dev(g) for g in gs])
+
+
 def test_blend():
     announce("blend")
     shapes = [(64, 96), (96, 64)]
