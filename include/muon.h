@@ -164,22 +164,26 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
 
 /* Graph capture of a step (page "Training NanoGPT in 39.9 Seconds", Table A,
  * credits capturing the training step as a device graph with part of the
- * end-to-end gain).  muon_step enqueues only kernel launches, except that it
- * first uploads a per-workspace descriptor table (matrix pointers, shapes,
- * tile offsets) whenever that table changes, which synchronises the stream.
- * muon_step_prepare validates the arguments exactly as muon_step does and
- * makes that table resident for these params/grads/state buffers, without
- * launching anything or touching the counters.  After it, a muon_step with
- * the same buffers can be captured (hipStreamBeginCapture, or a framework's
- * graph capture) on `stream`; a captured call whose table is not resident
- * returns MUON_E_CAPTURE and enqueues nothing.
+ * end-to-end gain).  Besides its kernel launches, muon_step enqueues one
+ * host-to-device copy of a per-workspace descriptor table (matrix pointers,
+ * shapes, tile offsets) from pinned staging memory, on every call; it does
+ * not synchronise the stream.  Under capture no copy is made: the table must
+ * already be in the workspace.  muon_step_prepare validates the arguments
+ * exactly as muon_step does and sends that table for these
+ * params/grads/state buffers, without launching anything or touching the
+ * counters.  After it, a muon_step with the same buffers can be captured
+ * (hipStreamBeginCapture, or a framework's graph capture) on `stream`; a
+ * captured call whose table is not resident returns MUON_E_CAPTURE and
+ * enqueues nothing.
  * A replay repeats the captured step on the same buffers with the captured
- * scalars: lr, wd, beta, coefficients, options, and the weight-average flags
- * derived from the counters (whether this step is averaged, and whether it is
- * the first averaged step).  The capturing call advances step/ema_count once
- * as for an eager call; replays do not touch the host state, so the caller
- * advances the counters per replay and captures only steps whose flags repeat
- * (weight average disabled, or already started).  Same errors as muon_step. */
+ * scalars: lr, wd, beta, coefficients, options, the weight-average
+ * coefficients, and the flags derived from the counters (whether this step is
+ * averaged, and whether it is the first averaged step).  The capturing call
+ * advances step/ema_count once as for an eager call; replays do not touch the
+ * host state, so the caller advances the counters per replay and captures
+ * only steps whose flags and coefficients repeat (weight average disabled, or
+ * an exponential average already started; not MUON_AVG_WEIGHTED).  Same
+ * errors as muon_step. */
 int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state* st,
                       void* stream);
 
