@@ -7,6 +7,12 @@ by effective shape: momentum, norm, 5 x (Gram, polynomial, apply), update.
 Inputs are synthetic (seeded low-rank + noise gradients at entry RMS 1e-3,
 0.02 N(0,1) parameters) and resident in HBM before the timed region.
 
+`--workload` selects another configuration of the same step for measurement
+(the line's metric is the 124M set's; the others are timed the same way):
+gpt124m_anvil (fast/slow momentum, six map steps, cautious decay 0.1, EMA),
+gpt2p7b (32 layers x {4x 2560^2, 2560x10240, 10240x2560}, wd 1.6) and
+moe_share (64 experts x {2048x1408, 1408x2048} + 24 x 4 x 2048^2).
+
 Prints one JSON line.  Extra fields: NS TFLOP/s (symmetric flop count),
 per-kernel times, the roofline of the dominant kernel (the APPLY GEMM,
 timed live with HIP events around its launches in the timed region), the
@@ -29,7 +35,20 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_apply_gpt124m.json")
+WORKLOADS = {
+    "gpt124m": "gpt124m matrix set: 72 bf16 matrices (48x 768x768, 12x 768x3072, 12x 3072x768), "
+               "fp32 momentum, Muon step, 5 quintic Newton-Schulz iterations, grouped by shape",
+    "gpt124m_anvil": "gpt124m matrix set, ANVIL-style step: fast (0.9) and slow (0.99) momentum, "
+                     "6 quintic map iterations, cautious weight decay 0.1, EMA 0.99 from step 1",
+    "gpt2p7b": "2.7B matrix set: 192 bf16 matrices (128x 2560x2560, 32x 2560x10240, "
+               "32x 10240x2560), fp32 momentum, wd 1.6, 5 quintic iterations",
+    "moe_share": "MoE one-GPU share: 224 bf16 matrices (64x 2048x1408, 64x 1408x2048, "
+                 "96x 2048x2048), fp32 momentum, 5 quintic iterations",
+}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_apply_{workload}.json")
 
 
 def _src_hash() -> str:
@@ -40,11 +59,11 @@ def _src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(launch_flops_key: str):
+def _traffic(workload: str, launch_flops_key: str):
     """HBM bytes per APPLY launch from the committed counter runs, if they
     were taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -62,31 +81,53 @@ def apply_flops(shapes) -> float:
     return tot
 
 
-def elementwise_bytes(shapes):
-    """Algorithmic HBM bytes of the prepare and finish kernels (plain Muon,
-    bf16 params/grads/iterate, fp32 momentum): prepare reads G (2) and M (4),
-    writes M (4) and X0 (2); finish reads O (2) and W (2), writes W (2)."""
+def elementwise_bytes(shapes, ms):
+    """Algorithmic HBM bytes of the prepare and finish kernels (bf16
+    params/grads/iterate, fp32 state): prepare reads G (2) and M (4), writes
+    M (4) and X0 (2), plus S (4 + 4) with slow momentum; finish reads O (2) and
+    W (2), writes W (2), plus S (4) with cautious decay and E (4 + 4) with an
+    average."""
     n = sum(r * c for r, c in shapes)
-    return 12.0 * n, 6.0 * n
+    prep = 12.0 + (8.0 if ms.beta_slow >= 0 else 0.0)
+    fin = 6.0 + (4.0 if ms.cautious else 0.0) + (8.0 if ms.beta_ema >= 0 else 0.0)
+    return prep * n, fin * n
 
 
-def cpu_baseline(shapes, grads_bits, params_bits, coeffs, lr, wd, beta):
-    """The CPU oracle (fp64 numpy) on one full optimizer step of the same set."""
+def cpu_baseline(ms, coeffs, budget_s: float = 20.0):
+    """The CPU oracle (fp64 numpy) on the same step.  The 124M set runs one
+    whole step; for larger sets the oracle steps through the matrices in
+    order until `budget_s` seconds have passed and the rate is scaled by the
+    Newton-Schulz flop count of the whole set (stated in `sample`)."""
     import threadpoolctl
     from oracle import muon_oracle as orc
     from workloads import gen
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    grads = [gen.f32_from_bf16_bits(g) for g in grads_bits]
-    params = [gen.f32_from_bf16_bits(w).astype(np.float64) for w in params_bits]
-    st = orc.OracleState(shapes)
-    t0 = time.perf_counter()
-    orc.muon_step(params, grads, st, coeffs, lr, wd, beta, param_dtype="bf16", keep=False)
-    dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 5), "unit": "optimizer steps/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"one full step of the same {len(shapes)}-matrix set on the host "
-                      f"({dt:.2f} s, fp64 numpy/OpenBLAS)"}
+    vendor = ",".join(sorted({str(i.get("internal_api")) for i in info
+                              if i.get("user_api") == "blas"})) or "unknown"
+    shapes = list(ms.shapes)
+    total_fl = sum(orc.ns_flops_dense(r, c, ms.steps) for r, c in shapes)
+    done_fl, done, dt = 0.0, 0, 0.0
+    for i in range(len(shapes)):
+        (g, w), = gen.make_inputs(ms, seed=0, indices=[i])
+        st = orc.OracleState([shapes[i]], beta_slow=ms.beta_slow, beta_ema=ms.beta_ema,
+                             ema_start=ms.ema_start)
+        t0 = time.perf_counter()
+        orc.muon_step([gen.f32_from_bf16_bits(w).astype(np.float64)], [gen.f32_from_bf16_bits(g)],
+                      st, coeffs, ms.lr, ms.wd, ms.beta, param_dtype="bf16",
+                      cautious=ms.cautious, keep=False)
+        dt += time.perf_counter() - t0
+        done_fl += orc.ns_flops_dense(*shapes[i], ms.steps)
+        done += 1
+        if dt > budget_s:
+            break
+    est = dt * total_fl / done_fl
+    sample = (f"one full step of the same {len(shapes)}-matrix set on the host ({dt:.2f} s"
+              if done == len(shapes) else
+              f"{done} of the {len(shapes)} matrices of one step on the host ({dt:.2f} s), "
+              f"scaled to the whole set by Newton-Schulz flops (estimated {est:.1f} s per step")
+    return {"value": round(1.0 / est, 5), "unit": "optimizer steps/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample + f", fp64 numpy, BLAS {vendor})"}
 
 
 def _events_ms(fn, reps):
@@ -166,6 +207,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="gpt124m", choices=sorted(WORKLOADS),
+                    help="matrix set and options of the step (default: the 124M set)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -189,20 +232,28 @@ def main():
         print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
         return
 
-    ms = gen.SETS["gpt124m"]
+    ms = gen.SETS[args.workload]
     shapes = list(ms.shapes)
     coeffs = gen.coeff_table(ms.coeffs, ms.steps)
-    inputs = gen.make_inputs(ms, seed=0)
-    grads_bits = [g for g, _ in inputs]
-    params_bits = [w for _, w in inputs]
+    if ms.numel <= 200_000_000:
+        inputs = gen.make_inputs(ms, seed=0)
 
-    def to_dev(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        def to_dev(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    params = [to_dev(w) for w in params_bits]
-    grads = [to_dev(g) for g in grads_bits]
+        params = [to_dev(w) for _, w in inputs]
+        grads = [to_dev(g) for g, _ in inputs]
+        del inputs
+    else:
+        # large sets: the same recipe drawn on the device
+        params = [gen.torch_param_matrix(r, c, 0, i, dev, dtype=torch.bfloat16)
+                  for i, (r, c) in enumerate(shapes)]
+        grads = [gen.torch_grad_matrix(r, c, 0, 0, i, dev, rms=ms.grad_rms, dtype=torch.bfloat16)
+                 for i, (r, c) in enumerate(shapes)]
     opt = mo.Muon(params, lr=ms.lr, wd=ms.wd, beta=ms.beta, steps=ms.steps, coeffs=coeffs,
-                  ns_dtype="bf16")
+                  ns_dtype="bf16", beta_slow=None if ms.beta_slow < 0 else ms.beta_slow,
+                  beta_ema=None if ms.beta_ema < 0 else ms.beta_ema, ema_start=ms.ema_start,
+                  cautious=ms.cautious)
     plan = mo.plan_info(shapes, ms.steps, coeffs)
     stream = torch.cuda.current_stream()
 
@@ -214,17 +265,17 @@ def main():
     # launch stream
     n_apply = args.steps * ms.steps
     mo.probe_arm("apply", n_apply)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
+    ev[0].record(stream)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for k in range(args.steps):
         opt.step(grads)
-    e1.record(stream)
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
     apply_ms = mo.probe_read(n_apply)
     mo.probe_disarm()
 
@@ -244,33 +295,35 @@ def main():
     # the same step captured once as a device graph and replayed (not part of
     # `value`); and the single 256x512 fp32 matrix, eager and replayed, where
     # launch latency dominates
-    graph_ms = time_graph(opt, grads, args.steps)
+    graph_ms = time_graph(opt, grads, args.steps) if ms.beta_ema < 0 or opt.ema_count > 0 else None
     c1 = single_matrix_times(gen, mo, dev, args.steps)
     adamw = adamw_times(gen, mo, dev, max(args.steps, 20))
 
     sym, dense = gen.ns_flops(shapes, ms.steps)
     a_flops = apply_flops(shapes)
     a_tf = a_flops / (phase_ms["apply"] * 1e-3) / 1e12
-    key = f"gpt124m:{ms.steps}:{ms.coeffs}"
-    traffic = _traffic(key)
-    prep_b, fin_b = elementwise_bytes(shapes)
+    key = f"{args.workload}:{ms.steps}:{ms.coeffs}"
+    traffic = _traffic(args.workload, key)
+    prep_b, fin_b = elementwise_bytes(shapes, ms)
     steps_per_s = 1000.0 / ms_step
     out = {
-        "metric": "optimizer steps/sec + NS TFLOP/s (% MFMA peak), 124M-GPT matrix set, 1 GPU",
+        "metric": "optimizer steps/sec + NS TFLOP/s (% MFMA peak), 124M-GPT matrix set, 1 GPU"
+                  if args.workload == "gpt124m" else
+                  f"optimizer steps/sec + NS TFLOP/s (% MFMA peak), {args.workload} matrix set, 1 GPU",
         "value": round(steps_per_s, 3),
         "unit": "optimizer steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_median_p90": [round(float(np.percentile(per_step, q)), 4)
+                                       for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded low-rank+noise gradients, random-init bf16 parameters)",
-        "config": {"workload": "gpt124m matrix set: 72 bf16 matrices (48x 768x768, "
-                               "12x 768x3072, 12x 3072x768), fp32 momentum, Muon step, "
-                               "5 quintic Newton-Schulz iterations, grouped by shape",
+        "config": {"workload": WORKLOADS[args.workload],
                    "matrices": len(shapes), "elements": int(sum(r * c for r, c in shapes)),
                    "ns_steps": ms.steps, "coeffs": "quintic (15/8, -10/8, 3/8)",
                    "groups": plan["groups"], "tile": plan["tile"],
@@ -292,8 +345,7 @@ def main():
         "adamw": adamw,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shapes, grads_bits, params_bits, coeffs, ms.lr,
-                                           ms.wd, ms.beta)
+        out["cpu_baseline"] = cpu_baseline(ms, coeffs)
     print(json.dumps(out), flush=True)
 
 
