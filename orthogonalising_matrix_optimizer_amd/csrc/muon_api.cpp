@@ -48,7 +48,8 @@ struct Plan {
   int waves = 4;
   // block order per phase (GRAM, POLY, APPLY): bit 0 plain order (no per-XCD
   // tile ranges), bit 1 row-major APPLY tiles (else groups of four row
-  // panels), bit 2 whole matrices dealt to XCDs (matrix j on XCD j mod 8)
+  // panels), bit 2 whole matrices dealt to XCDs (matrix j on XCD j mod 8),
+  // bit 3 APPLY tiles column panel by column panel
   int order[3] = {1, 1, 1};
   std::vector<int> launch_groups;   // groups in launch order: costliest tiles first
   std::vector<GroupPlan> groups;
@@ -59,15 +60,16 @@ struct Plan {
 
 // Whether dealing whole matrices to the eight XCDs (matrix j of every group
 // on XCD j mod 8) gives each XCD within 5% of the mean work in every launch
-// set of a symmetric phase (0 GRAM, 1 POLY).
+// set of a phase (0 GRAM, 1 POLY, 2 APPLY).
 bool xcd_deal_balanced(const Plan& p, int phase) {
   for (size_t g0 = 0; g0 < p.groups.size(); g0 += kMaxGroups) {
     const size_t g1 = std::min(p.groups.size(), g0 + kMaxGroups);
     double cost[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tot = 0;
     for (size_t gi = g0; gi < g1; ++gi) {
       const GroupPlan& g = p.groups[p.launch_groups[gi]];
-      const int tm = g.mp / p.ts;
-      const double unit = double(tm) * (tm + 1) / 2 * (phase == 0 ? g.np : g.mp);
+      const int tm = g.mp / p.ts, tn = g.np / p.ts;
+      const double unit = phase == 2 ? double(tm) * tn * g.mp
+                                     : double(tm) * (tm + 1) / 2 * (phase == 0 ? g.np : g.mp);
       const int c = int(g.mats.size());
       for (int x = 0; x < 8; ++x) cost[x] += ((c + 7 - x) / 8) * unit;
       tot += c * unit;
@@ -191,14 +193,18 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
     return p.groups[a].np > p.groups[b].np;
   });
   // GRAM and POLY: whole matrices per XCD when that keeps the XCDs balanced
-  // (tiles of one matrix share operand panels in that XCD's L2)
+  // (tiles of one matrix share operand panels in that XCD's L2).  APPLY
+  // likewise, walking each matrix one column panel at a time (all row panels
+  // of a column in turn), so that the blocks in flight on an XCD share a few
+  // X column panels and the matrix's B row panels
   for (int ph = 0; ph < 2; ++ph)
     if (xcd_deal_balanced(p, ph)) p.order[ph] = 4;
+  if (xcd_deal_balanced(p, 2)) p.order[2] = 4 | 8;
   // MUON_GEMM_ORDER="g,p,a" overrides the per-phase order bits (experiments)
   if (const char* e = std::getenv("MUON_GEMM_ORDER")) {
     int v[3] = {p.order[0], p.order[1], p.order[2]};
     if (std::sscanf(e, "%d,%d,%d", &v[0], &v[1], &v[2]) == 3)
-      for (int k = 0; k < 3; ++k) p.order[k] = v[k] & 7;
+      for (int k = 0; k < 3; ++k) p.order[k] = v[k] & 15;
   }
   p.pprefix.assign(n + 1, 0);
   p.fprefix.assign(n + 1, 0);

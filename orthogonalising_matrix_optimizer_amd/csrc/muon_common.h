@@ -93,7 +93,9 @@ struct GemmArgs {
   float cbb;              // APPLY: multiplier of the product (1, or b when B = bA)
   float eps;
   int32_t order;          // bit 0: plain block order (no XCD grouping);
-                          // bit 1: row-major APPLY tile order
+                          // bit 1: row-major APPLY tile order;
+                          // bit 2: whole matrices dealt to XCDs (j on j mod 8);
+                          // bit 3: APPLY tiles by column panel
 };
 
 }  // namespace muon

@@ -740,7 +740,13 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
     tile = local - mat * G.tiles;
   }
   int tP, tQ;
-  if (MODE == APPLY && (args.order & 2)) {
+  if (MODE == APPLY && (args.order & 8)) {
+    // column panels in turn, all row panels of each: the blocks of an XCD then
+    // share a few X column panels and every B row panel of the matrix
+    const int tm = G.mp / TS;
+    tQ = tile % tm;
+    tP = tile / tm;
+  } else if (MODE == APPLY && (args.order & 2)) {
     tP = tile % (G.np / TS);
     tQ = tile / (G.np / TS);
   } else if (MODE == APPLY) {
