@@ -377,9 +377,13 @@ __device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, in
   // stages still in flight
   lds_barrier();
   if (k + NST - 1 < nk) gemm_issue<XDT, MODE, TS, NW>(la, lb, k + NST - 1, wave, fill);
+  // GRAM: the wave in its MFMA run takes issue priority over the other wave
+  // of its SIMD (measured: GRAM 2.5 % faster; neutral for POLY, APPLY)
+  if constexpr (MODE == GRAM) __builtin_amdgcn_s_setprio(1);
   gemm_compute<XDT, MODE, TS, WGP, WGQ, 0>(cur, cur + OPB, lane, wr, wc, acc);
   if constexpr (XDT == kBF16)
     gemm_compute<XDT, MODE, TS, WGP, WGQ, 1>(cur, cur + OPB, lane, wr, wc, acc);
+  if constexpr (MODE == GRAM) __builtin_amdgcn_s_setprio(0);
 }
 
 // ---- input term and staged output of 256-wide bf16 tiles
