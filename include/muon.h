@@ -287,7 +287,9 @@ size_t muon_adamw_workspace_bytes(int32_t n);
  * nearest even), grads[i] of the same numel (any element type).  All of
  * params, grads, m, v and the workspace must be pairwise disjoint.  Errors as
  * for muon_step (MUON_E_SHAPE: negative or mismatched numel; MUON_E_HPARAM:
- * the ranges above); n == 0 only advances the counter. */
+ * the ranges above); n == 0 only advances the counter.  The bias terms
+ * change with every step, so a call on a stream under graph capture returns
+ * MUON_E_CAPTURE and enqueues nothing. */
 int muon_adamw_step(const muon_vec* params, const muon_vec* grads, muon_adamw_state* st,
                     const muon_adamw_hparams* hp, void* stream);
 

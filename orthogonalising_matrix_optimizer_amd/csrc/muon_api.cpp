@@ -932,6 +932,11 @@ int muon_adamw_step(const muon_vec* params, const muon_vec* grads, muon_adamw_st
   std::memcpy(bytes.data() + adamw_off_prefix(n), prefix.data(), sizeof(int64_t) * size_t(n + 1));
   std::lock_guard<std::mutex> lk(g_mu);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // the bias terms change with every step, so a replayed capture would
+  // repeat stale ones: refuse capture
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MUON_E_HIP;
+  if (cs != hipStreamCaptureStatusNone) return MUON_E_CAPTURE;
   int rc;
   if ((rc = upload_table(st->workspace, bytes, s)) != MUON_OK) return rc;
 

@@ -150,3 +150,27 @@ def test_repeatable_bit_for_bit():
     torch.cuda.synchronize()
     for x, y in zip(pa + a.m + a.v, pb + b.m + b.v):
         assert torch.equal(x, y)
+
+
+def test_capture_is_refused():
+    """The bias terms change every step: a captured AdamW step would replay
+    stale ones, so the call refuses capture and leaves everything as it was."""
+    announce("adamw refuses graph capture")
+    bf = torch.bfloat16
+    opt, params, grads, _ = _make([5000], [bf], [bf], seed=6)
+    g = grads(0)
+    opt.step(g)
+    torch.cuda.synchronize()
+    before = [host(x).copy() for x in params + opt.m + opt.v]
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(mo._lib.MuonError) as err:
+        with torch.cuda.graph(graph):
+            opt.step(g)
+    assert err.value.code == mo._lib.CODES["MUON_E_CAPTURE"]
+    torch.cuda.synchronize()
+    assert opt.step_count == 1
+    for a, b in zip(before, [host(x) for x in params + opt.m + opt.v]):
+        np.testing.assert_array_equal(a, b)
+    opt.step(g)                       # eager steps still work afterwards
+    torch.cuda.synchronize()
+    assert opt.step_count == 2
