@@ -182,8 +182,9 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
  * advances step/ema_count once as for an eager call; replays do not touch the
  * host state, so the caller advances the counters per replay and captures
  * only steps whose flags and coefficients repeat (weight average disabled, or
- * an exponential average already started; not MUON_AVG_WEIGHTED).  Same
- * errors as muon_step. */
+ * an exponential average already started).  A captured step that would fold
+ * into a MUON_AVG_WEIGHTED average returns MUON_E_CAPTURE (its coefficients
+ * change every step).  Same errors as muon_step. */
 int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state* st,
                       void* stream);
 

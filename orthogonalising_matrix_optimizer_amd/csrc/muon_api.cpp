@@ -603,6 +603,13 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (weighted && !prepare_only) {
+    // the weighted average's coefficients change with every step: a replayed
+    // capture would repeat stale ones
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MUON_E_HIP;
+    if (cs != hipStreamCaptureStatusNone) return MUON_E_CAPTURE;
+  }
   if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
   if (prepare_only) return MUON_OK;
 
