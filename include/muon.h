@@ -51,7 +51,10 @@ enum { MUON_BF16 = 0, MUON_F32 = 1 };
 enum {
   MUON_OK = 0,
   MUON_E_NULL = 1,       /* a required pointer is NULL                          */
-  MUON_E_SHAPE = 2,      /* n < 0, rows/cols < 1, ld < cols, shapes differ      */
+  MUON_E_SHAPE = 2,      /* n < 0, rows/cols < 1, ld < cols, shapes differ, or
+                            a matrix too large (its padded wide iterate, the
+                            shape rounded up to the tile, must stay below
+                            4 GiB of the Newton-Schulz element type)          */
   MUON_E_DTYPE = 3,      /* unknown element type                                */
   MUON_E_COEFFS = 4,     /* steps outside [0, MUON_MAX_STEPS] or non-finite a,b,c */
   MUON_E_HPARAM = 5,     /* non-finite lr/wd/eps, beta outside [0,1), bad option */

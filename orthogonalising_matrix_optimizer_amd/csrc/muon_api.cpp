@@ -56,6 +56,8 @@ struct Plan {
   std::vector<int> mat_group, mat_slot;
   size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
   std::vector<int64_t> pprefix, fprefix;
+  // every padded iterate is addressable by the GEMMs' 32-bit buffer offsets
+  bool fits = true;
 };
 
 // Whether dealing whole matrices to the eight XCDs (matrix j of every group
@@ -171,6 +173,7 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
     g.x_elems = int64_t(g.mp) * g.np;
     g.a_elems = int64_t(g.mp) * g.mp;
     g.npart = (g.mp / kEw) * (g.np / kEw);
+    if (uint64_t(g.mp) * uint64_t(g.np) * uint64_t(es) >= (uint64_t(1) << 32)) p.fits = false;
     const size_t cnt = g.mats.size();
     g.off_x0 = off; off = align_up(off + cnt * g.x_elems * es, kAlign);
     g.off_x1 = off; off = align_up(off + cnt * g.x_elems * es, kAlign);
@@ -227,9 +230,8 @@ const Plan& get_plan(const int64_t* rows, const int64_t* cols, int n, int xdt) {
   std::vector<int64_t> key(2 * size_t(n));
   for (int i = 0; i < n; ++i) { key[2 * i] = rows[i]; key[2 * i + 1] = cols[i]; }
   const char* e = std::getenv("MUON_TILE");
-  const char* w = nullptr;
   const char* o = std::getenv("MUON_GEMM_ORDER");
-  const std::string tile_env = std::string(e ? e : "-") + "/" + (w ? w : "-") + "/" + (o ? o : "-");
+  const std::string tile_env = std::string(e ? e : "-") + "/" + (o ? o : "-");
   auto k = std::make_tuple(std::move(key), xdt, tile_env);
   auto it = g_plans.find(k);
   if (it != g_plans.end()) return it->second;
@@ -506,7 +508,8 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n, const muon_option
     cols[i] = params[i].cols;
   }
   std::lock_guard<std::mutex> lk(g_mu);
-  return get_plan(rows.data(), cols.data(), n, xdt).total;
+  const Plan& p = get_plan(rows.data(), cols.data(), n, xdt);
+  return p.fits ? p.total : 0;
 }
 
 namespace {
@@ -573,6 +576,7 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   if (!st->workspace) return MUON_E_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_mu);
   const Plan& p = get_plan(rows.data(), cols.data(), n, o.ns_dtype);
+  if (!p.fits) return MUON_E_SHAPE;
   if (st->workspace_bytes < p.total) return MUON_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(st->workspace) % kAlign) return MUON_E_ALIGN;
   add_range(ranges, st->workspace, p.total);
@@ -701,6 +705,7 @@ int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const
   if (!workspace) return MUON_E_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_mu);
   const Plan& p = get_plan(rows.data(), cols.data(), n, o.ns_dtype);
+  if (!p.fits) return MUON_E_SHAPE;
   if (workspace_bytes < p.total) return MUON_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return MUON_E_ALIGN;
   add_range(ranges, workspace, p.total);
@@ -774,6 +779,7 @@ int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state
   if (!st->workspace) return MUON_E_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_mu);
   const Plan& p = get_plan(rows.data(), cols.data(), n, st->opt.ns_dtype == MUON_F32 ? MUON_F32 : MUON_BF16);
+  if (!p.fits) return MUON_E_SHAPE;
   if (st->workspace_bytes < p.total) return MUON_E_WORKSPACE;
   add_range(ranges, st->workspace, p.total);
   if (overlaps(ranges)) return MUON_E_ALIAS;
@@ -857,6 +863,7 @@ int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt, i
   }
   std::lock_guard<std::mutex> lk(g_mu);
   const Plan& p = get_plan(rows.data(), cols.data(), n, xdt);
+  if (!p.fits) return MUON_E_SHAPE;
   if (n_groups) *n_groups = int(p.groups.size());
   if (tiles)
     for (int i = 0; i < std::min<int>(cap, int(p.groups.size())); ++i) tiles[i] = p.ts;

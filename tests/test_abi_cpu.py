@@ -398,3 +398,16 @@ def test_weighted_average_validation(lib):
     st.opt.avg_mode = 7
     assert lib.muon_step(None, None, st, _coeffs(), 5, 0.02, 0.0, 0.95, None) == \
         E["MUON_E_HPARAM"]
+
+
+def test_rejects_matrices_beyond_32_bit_offsets(lib):
+    """The GEMMs address one matrix's padded iterate with 32-bit offsets: a
+    bf16 60000 x 60000 matrix (about 7.2 GB padded) is rejected, one of
+    30000 x 60000 (3.6 GB) is planned."""
+    big = _lib.mat_array([(0, 60000, 60000, 60000, _lib.MUON_BF16)])
+    ok = _lib.mat_array([(0, 30000, 60000, 60000, _lib.MUON_BF16)])
+    opt = _lib.default_options()
+    assert lib.muon_workspace_bytes(big, 1, opt, 5) == 0
+    assert lib.muon_workspace_bytes(ok, 1, opt, 5) > 3 * 2 ** 30
+    opt.ns_dtype = _lib.MUON_F32
+    assert lib.muon_workspace_bytes(ok, 1, opt, 5) == 0
