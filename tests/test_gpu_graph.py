@@ -94,3 +94,29 @@ def test_graph_refused_before_average_starts():
     with pytest.raises(ValueError):
         opt.graph(_grads(8, 0))
     assert opt.step_count == 0
+
+
+def test_c_abi_refuses_capture_of_weighted_average_steps():
+    """The weighted average's coefficients change every step; muon_step
+    itself (not only the Python wrapper) refuses to be captured for such a
+    step, enqueues nothing and leaves the counters alone."""
+    announce("graph: C ABI refuses capture with the weighted average")
+    p = _params(9)
+    opt = mo.Muon(p, beta_ema=0.0, ema_start=1, avg="weighted")
+    g = _grads(9, 0)
+    opt.step(g)
+    torch.cuda.synchronize()
+    opt.step_prepare(g)
+    torch.cuda.synchronize()
+    before = [x.clone() for x in p]
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(mo._lib.MuonError) as err:
+        with torch.cuda.graph(graph):
+            code = opt.lib.muon_step(opt._pmats, opt._grad_mats(g), opt.state, opt._coeffs_c,
+                                     opt.steps, opt.lr, opt.wd, opt.beta,
+                                     torch.cuda.current_stream().cuda_stream)
+            mo._lib.check(code, "muon_step")
+    assert err.value.code == mo._lib.CODES["MUON_E_CAPTURE"]
+    torch.cuda.synchronize()
+    assert opt.step_count == 1 and opt.ema_count == 1
+    assert all(torch.equal(a, b) for a, b in zip(before, p))
