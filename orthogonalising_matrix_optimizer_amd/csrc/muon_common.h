@@ -17,7 +17,8 @@
 
 namespace muon {
 
-constexpr int kThreads = 256;     // threads per block, every kernel
+constexpr int kThreads = 256;     // threads per block (elementwise kernels but prepare)
+constexpr int kPrepThreads = 512; // threads per block of the prepare kernel
 constexpr int kEw = 64;           // edge of the elementwise (prepare/finish) tiles
 // row strips of the elementwise kernels for matrices kept in their layout;
 // a strip holds as many elements as a tile, so both give the same partial count

@@ -64,13 +64,16 @@ __device__ __forceinline__ int find_mat(const int64_t* prefix, int n, int64_t b)
 }
 
 // Deterministic block sum: wave butterfly, then the four wave totals in order.
+template <int NW = 4>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  float s = ((red[0] + red[1]) + red[2]) + red[3];
+  float s = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) s = s + red[w];
   return s;
 }
 
@@ -208,11 +211,12 @@ __device__ __forceinline__ void store8(void* row, int dt, bool vec, int valid, f
 }
 
 // Matrix scale s = 1 / (sqrt(sum of partials) + eps); same order everywhere.
+template <int NT = kThreads>
 __device__ __forceinline__ float matrix_scale(const float* partials, int count, float eps,
                                               float* red) {
   float acc = 0.f;
-  for (int i = threadIdx.x; i < count; i += kThreads) acc += glb(partials)[i];
-  float s = block_sum(acc, red);
+  for (int i = threadIdx.x; i < count; i += NT) acc += glb(partials)[i];
+  float s = block_sum<NT / 64>(acc, red);
   return 1.0f / (sqrtf(s) + eps);
 }
 
@@ -223,24 +227,26 @@ __device__ __forceinline__ float matrix_scale(const float* partials, int count, 
 // 512-byte (fp32) row segments.  A strip holds as many elements as a 64 x 64
 // tile, so the strip count of the padded iterate equals its partial count.
 // Tall matrices keep 64 x 64 tiles, transposed through LDS.
-template <bool STEP, bool SLOW>
+template <bool STEP, bool SLOW, int NT>
 __device__ __forceinline__ void prepare_strip(const ElemArgs& a, const MatDesc& d, int local,
                                               float* red) {
+  constexpr int NP = kStripRows * 16 / NT;   // passes: rows of 16 lanes each
+  constexpr int RPP = NT / 16;               // rows per pass
   const int spr = d.np / kStripCols;
   const int si = local / spr, sj = local - si * spr;
   const int t = threadIdx.x, lr = t >> 4;
   const int sc = sj * kStripCols + (t & 15) * 8;
   const int gsz = d.gdt == kBF16 ? 2 : 4;
-  int sr[2], valid[2];
-  float g[2][8], m[2][8], sl[2][8];
+  int sr[NP], valid[NP];
+  float g[NP][8], m[NP][8], sl[NP][8];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    sr[ps] = si * kStripRows + lr + 16 * ps;
+  for (int ps = 0; ps < NP; ++ps) {
+    sr[ps] = si * kStripRows + lr + RPP * ps;
     valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
   }
   // every load of the strip in flight before any arithmetic
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     if (valid[ps] <= 0) continue;
     const char* grow = static_cast<const char*>(d.g) + (static_cast<int64_t>(sr[ps]) * d.ldg + sc) * gsz;
     load8(grow, d.gdt, d.gvec, valid[ps], g[ps]);
@@ -253,7 +259,7 @@ __device__ __forceinline__ void prepare_strip(const ElemArgs& a, const MatDesc& 
   float ss = 0.f;
   const int xsz = a.xdt == kBF16 ? 2 : 4;
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     float u[8];
     if (valid[ps] <= 0) {
 #pragma unroll
@@ -281,13 +287,15 @@ __device__ __forceinline__ void prepare_strip(const ElemArgs& a, const MatDesc& 
     char* xrow = static_cast<char*>(d.x0) + (static_cast<int64_t>(sr[ps]) * d.np + sc) * xsz;
     store8(xrow, a.xdt, true, 8, u);
   }
-  const float tot = block_sum(ss, red);
+  const float tot = block_sum<NT / 64>(ss, red);
   if (t == 0) glb(d.partials)[local] = tot;
 }
 
-template <bool STEP, bool CAUT, bool EMA>
+template <bool STEP, bool CAUT, bool EMA, int NT>
 __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d, int local,
                                              float* red) {
+  constexpr int NP = kStripRows * 16 / NT;   // passes: rows of 16 lanes each
+  constexpr int RPP = NT / 16;               // rows per pass
   const int spr = (d.cols + kStripCols - 1) / kStripCols;
   const int si = local / spr, sj = local - si * spr;
   const int t = threadIdx.x, lr = t >> 4;
@@ -295,16 +303,16 @@ __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d
   const int esz = a.xdt == kBF16 ? 2 : 4;
   const int wsz = d.wdt == kBF16 ? 2 : 4;
   const void* xb = a.final_buf ? d.x1 : d.x0;
-  int sr[2], valid[2];
-  float o[2][8], w[2][8], sl[2][8], e[2][8];
+  int sr[NP], valid[NP];
+  float o[NP][8], w[NP][8], sl[NP][8], e[NP][8];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    sr[ps] = si * kStripRows + lr + 16 * ps;
+  for (int ps = 0; ps < NP; ++ps) {
+    sr[ps] = si * kStripRows + lr + RPP * ps;
     valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
   }
   constexpr bool upd = STEP;
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     if (valid[ps] <= 0) continue;
     // X rows sr < mp and columns sc .. sc+7 < np: in bounds
     load8(static_cast<const char*>(xb) + (static_cast<int64_t>(sr[ps]) * d.np + sc) * esz, a.xdt,
@@ -318,14 +326,14 @@ __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d
     }
   }
   if (a.scale_o) {
-    const float s = matrix_scale(d.partials, d.npartials, a.eps, red);
+    const float s = matrix_scale<NT>(d.partials, d.npartials, a.eps, red);
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
+    for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[ps][k] = s * o[ps][k];
   }
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     if (valid[ps] <= 0) continue;
     char* wrow = static_cast<char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz;
     if (!upd) {                   // orthogonalize: out = O
@@ -389,16 +397,18 @@ __device__ __forceinline__ void blend_strip(const ElemArgs& a, const MatDesc& d,
 // t / 8 + 32 and writes 8 consecutive X0 elements of rows t / 8 and t / 8 + 32;
 // both LDS patterns touch 64 distinct banks per wave.
 // STEP: optimizer step (else orthogonalize input); SLOW: slow momentum.
-template <bool STEP, bool SLOW>
-__global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
+template <bool STEP, bool SLOW, int NT>
+__global__ __launch_bounds__(NT) void k_prepare(ElemArgs a) {
+  constexpr int NP = kEw * 8 / NT;   // passes of NT / 8 rows
+  constexpr int RPP = NT / 8;
   __shared__ float tile[kEw][kEw + 1];
-  __shared__ float red[4];
+  __shared__ float red[NT / 64];
   const int64_t b = blockIdx.x;
   const int mi = find_mat(a.prefix, a.nmats, b);
   const MatDesc& d = a.mats[mi];
   const int local = static_cast<int>(b - a.prefix[mi]);
   if (!d.tall) {
-    prepare_strip<STEP, SLOW>(a, d, local, red);
+    prepare_strip<STEP, SLOW, NT>(a, d, local, red);
     return;
   }
   const int tpr = d.np / kEw;
@@ -406,15 +416,15 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
   const int t = threadIdx.x, lr = t >> 3, lc = (t & 7) * 8;
   const int sc = ti * kEw + lc;
   const int gsz = d.gdt == kBF16 ? 2 : 4;
-  int sr[2], valid[2];
-  float g[2][8], m[2][8], sl[2][8];
+  int sr[NP], valid[NP];
+  float g[NP][8], m[NP][8], sl[NP][8];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    sr[ps] = tj * kEw + lr + 32 * ps;
+  for (int ps = 0; ps < NP; ++ps) {
+    sr[ps] = tj * kEw + lr + RPP * ps;
     valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
   }
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     if (valid[ps] <= 0) continue;
     const char* grow = static_cast<const char*>(d.g) + (static_cast<int64_t>(sr[ps]) * d.ldg + sc) * gsz;
     load8(grow, d.gdt, d.gvec, valid[ps], g[ps]);
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
   }
   float ss = 0.f;
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     float u[8];
     if (valid[ps] <= 0) {
 #pragma unroll
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       ss = ss + u[k] * u[k];
-      tile[lr + 32 * ps][lc + k] = u[k];
+      tile[lr + RPP * ps][lc + k] = u[k];
     }
   }
   __syncthreads();
@@ -459,14 +469,14 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
   // rows), ld = np: always in bounds, padding gets zeros
   const int xsz = a.xdt == kBF16 ? 2 : 4;
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     float u[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) u[k] = tile[lc + k][lr + 32 * ps];
-    const int64_t xi = static_cast<int64_t>(ti * kEw + lr + 32 * ps) * d.np + tj * kEw + lc;
+    for (int k = 0; k < 8; ++k) u[k] = tile[lc + k][lr + RPP * ps];
+    const int64_t xi = static_cast<int64_t>(ti * kEw + lr + RPP * ps) * d.np + tj * kEw + lc;
     store8(static_cast<char*>(d.x0) + xi * xsz, a.xdt, true, 8, u);
   }
-  const float tot = block_sum(ss, red);
+  const float tot = block_sum<NT / 64>(ss, red);
   if (t == 0) glb(d.partials)[local] = tot;
 }
 
@@ -475,16 +485,18 @@ __global__ __launch_bounds__(kThreads) void k_prepare(ElemArgs a) {
 // the transpose of the X tile at (rows fj*64.., columns fi*64..), staged
 // through LDS as in k_prepare.
 // STEP: optimizer update (else store O); CAUT: cautious mask; EMA: weight average.
-template <bool STEP, bool CAUT, bool EMA>
-__global__ __launch_bounds__(kThreads) void k_finish(ElemArgs a) {
+template <bool STEP, bool CAUT, bool EMA, int NT>
+__global__ __launch_bounds__(NT) void k_finish(ElemArgs a) {
+  constexpr int NP = kEw * 8 / NT;   // passes of NT / 8 rows
+  constexpr int RPP = NT / 8;
   __shared__ float tile[kEw][kEw + 1];
-  __shared__ float red[4];
+  __shared__ float red[NT / 64];
   const int64_t b = blockIdx.x;
   const int mi = find_mat(a.prefix, a.nmats, b);
   const MatDesc& d = a.mats[mi];
   const int local = static_cast<int>(b - a.prefix[mi]);
   if (!d.tall) {
-    finish_strip<STEP, CAUT, EMA>(a, d, local, red);
+    finish_strip<STEP, CAUT, EMA, NT>(a, d, local, red);
     return;
   }
   const int tpr = (d.cols + kEw - 1) / kEw;
@@ -494,19 +506,19 @@ __global__ __launch_bounds__(kThreads) void k_finish(ElemArgs a) {
   const int wsz = d.wdt == kBF16 ? 2 : 4;
   const void* xb = a.final_buf ? d.x1 : d.x0;
   const int sc = fj * kEw + lc;
-  int sr[2], valid[2];
-  float x[2][8], w[2][8], sl[2][8], e[2][8];
+  int sr[NP], valid[NP];
+  float x[NP][8], w[NP][8], sl[NP][8], e[NP][8];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    sr[ps] = fi * kEw + lr + 32 * ps;
+  for (int ps = 0; ps < NP; ++ps) {
+    sr[ps] = fi * kEw + lr + RPP * ps;
     valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
     // X rows fj*64 + lr (+32) < mp, columns fi*64 + lc .. < np: in bounds
-    const int64_t xi = static_cast<int64_t>(fj * kEw + lr + 32 * ps) * d.np + fi * kEw + lc;
+    const int64_t xi = static_cast<int64_t>(fj * kEw + lr + RPP * ps) * d.np + fi * kEw + lc;
     load8(static_cast<const char*>(xb) + xi * esz, a.xdt, true, 8, x[ps]);
   }
   if (STEP) {
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
+    for (int ps = 0; ps < NP; ++ps) {
       if (valid[ps] <= 0) continue;
       const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
       load8(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
@@ -516,24 +528,24 @@ __global__ __launch_bounds__(kThreads) void k_finish(ElemArgs a) {
     }
   }
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps)
+  for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) tile[lr + 32 * ps][lc + k] = x[ps][k];
+    for (int k = 0; k < 8; ++k) tile[lr + RPP * ps][lc + k] = x[ps][k];
   __syncthreads();
-  float o[2][8];
+  float o[NP][8];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps)
+  for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o[ps][k] = tile[lc + k][lr + 32 * ps];
+    for (int k = 0; k < 8; ++k) o[ps][k] = tile[lc + k][lr + RPP * ps];
   if (a.scale_o) {
-    const float s = matrix_scale(d.partials, d.npartials, a.eps, red);
+    const float s = matrix_scale<NT>(d.partials, d.npartials, a.eps, red);
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
+    for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[ps][k] = s * o[ps][k];
   }
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
     if (valid[ps] <= 0) continue;
     char* wrow = static_cast<char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz;
     if (!STEP) {                  // orthogonalize: out = O
@@ -643,28 +655,32 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
 hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(blocks));
+  constexpr int NT = kPrepThreads;
   if (a.mode == 1)
-    hipLaunchKernelGGL((k_prepare<false, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_prepare<false, false, NT>), grid, dim3(NT), 0, s, a);
   else if (a.use_slow)
-    hipLaunchKernelGGL((k_prepare<true, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_prepare<true, true, NT>), grid, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_prepare<true, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_prepare<true, false, NT>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_finish(const ElemArgs& a, int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>(blocks)), blk(kThreads);
+  // block size per option set (measured): the plain update streams two
+  // arrays and runs best with 256 threads; with the slow momentum and the
+  // average it streams five and runs best with 512
+  const dim3 grid(static_cast<uint32_t>(blocks));
   if (a.mode == 1)
-    hipLaunchKernelGGL((k_finish<false, false, false>), grid, blk, 0, s, a);
+    hipLaunchKernelGGL((k_finish<false, false, false, 256>), grid, dim3(256), 0, s, a);
   else if (a.cautious && a.ema_on)
-    hipLaunchKernelGGL((k_finish<true, true, true>), grid, blk, 0, s, a);
+    hipLaunchKernelGGL((k_finish<true, true, true, 512>), grid, dim3(512), 0, s, a);
   else if (a.cautious)
-    hipLaunchKernelGGL((k_finish<true, true, false>), grid, blk, 0, s, a);
+    hipLaunchKernelGGL((k_finish<true, true, false, 512>), grid, dim3(512), 0, s, a);
   else if (a.ema_on)
-    hipLaunchKernelGGL((k_finish<true, false, true>), grid, blk, 0, s, a);
+    hipLaunchKernelGGL((k_finish<true, false, true, 512>), grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((k_finish<true, false, false>), grid, blk, 0, s, a);
+    hipLaunchKernelGGL((k_finish<true, false, false, 256>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
