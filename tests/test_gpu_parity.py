@@ -436,3 +436,47 @@ def test_twin_optimizers_stay_bitwise_equal(tile, ns):
                 assert torch.equal(opts[0].update[i], opts[k].update[i]), (t, k, i)
                 assert torch.equal(params[0][i], params[k][i]), (t, k, i)
                 assert torch.equal(opts[0].mom[i], opts[k].mom[i]), (t, k, i)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_views_match_oracle(dtype):
+    """Parameters and gradients that are column windows of wider buffers:
+    row pitch larger than the width, odd pitches and bases that break 16-byte
+    alignment (the elementwise kernels' scalar paths), tall and wide.  The
+    step must match the oracle and leave the rest of each buffer untouched."""
+    announce(f"strided views {dtype}")
+    shapes = [(200, 333), (333, 200), (64, 130)]
+    pitches = [1001, 257, 136]
+    gs, ws = _make(shapes, dtype, rms=None if dtype == "f32" else 1e-3)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    sentinel = 7.0
+    bufs, params, grads = [], [], []
+    for (r, c), ld, g, w in zip(shapes, pitches, gs, ws):
+        pb = torch.full((r, ld), sentinel, dtype=tdt, device="cuda")
+        gb = torch.full((r, ld + 5), sentinel, dtype=tdt, device="cuda")
+        pv, gv = pb[:, 3:3 + c], gb[:, 1:1 + c]
+        pv.copy_(_dev(w))
+        gv.copy_(_dev(g))
+        bufs.append((pb, gb, 3, 1))
+        params.append(pv)
+        grads.append(gv)
+    lr, wd, beta = 0.02, 0.1, 0.95
+    opt = mo.Muon(params, lr=lr, wd=wd, beta=beta, steps=5, coeffs="quintic", diagnostics=True)
+    opt.step(grads)
+    torch.cuda.synchronize()
+    st = orc.OracleState(shapes)
+    w0 = [_val(w).astype(np.float64) for w in ws]
+    lr32, wd32 = float(np.float32(lr)), float(np.float32(wd))
+    ref = orc.muon_step(w0, [_val(g) for g in gs], st, _table("quintic", 5), lr32, wd32, beta,
+                        param_dtype=dtype)
+    for i, (r, c) in enumerate(shapes):
+        np.testing.assert_array_equal(host(opt.mom[i]), st.mom[i])
+        O = host(opt.update[i])
+        assert orc.rel_fro(O, ref["O"][i]) <= TOL_BF16, shapes[i]
+        want = orc.store(orc.update_f32(w0[i], O, lr, wd), dtype)
+        np.testing.assert_array_equal(host(params[i]).astype(np.float64), want)
+        pb, gb, po, go = bufs[i]
+        hp, hg = host(pb), host(gb)
+        hp[:, po:po + c] = sentinel
+        hg[:, go:go + c] = sentinel
+        assert np.all(hp == sentinel) and np.all(hg == sentinel), shapes[i]
