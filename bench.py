@@ -152,9 +152,9 @@ def time_graph(opt, grads, reps):
     return round(_events_ms(g.replay, reps), 4)
 
 
-def single_matrix_times(gen, mo, dev, reps):
+def single_matrix_times(gen, mo, dev, reps, with_oracle=True):
     """One 256x512 fp32 matrix (five quintic iterations, bf16 operands): ms per
-    step eager and as a replayed graph."""
+    step eager and as a replayed graph, and the CPU oracle on one thread."""
     import torch
     ms = gen.SETS["single_256x512"]
     (g, w), = gen.make_inputs(ms, seed=0)
@@ -165,9 +165,24 @@ def single_matrix_times(gen, mo, dev, reps):
     for _ in range(5):
         opt.step(gr)
     eager = _events_ms(lambda: opt.step(gr), max(reps, 20))
-    return {"workload": "one 256x512 fp32 matrix, 5 quintic iterations, bf16 operands",
-            "eager_ms_per_step": round(eager, 4),
-            "graph_ms_per_step": time_graph(opt, gr, max(reps, 20))}
+    out = {"workload": "one 256x512 fp32 matrix, 5 quintic iterations, bf16 operands",
+           "eager_ms_per_step": round(eager, 4),
+           "graph_ms_per_step": time_graph(opt, gr, max(reps, 20))}
+    if with_oracle:
+        # the CPU oracle on the same matrix, BLAS limited to one thread
+        import threadpoolctl
+        from oracle import muon_oracle as orc
+        with threadpoolctl.threadpool_limits(limits=1, user_api="blas"):
+            coeffs = gen.coeff_table(ms.coeffs, ms.steps)
+            t = []
+            for _ in range(5):
+                st = orc.OracleState([ms.shapes[0]])
+                t0 = time.perf_counter()
+                orc.muon_step([w.astype(np.float64)], [g], st, coeffs, ms.lr, ms.wd, ms.beta,
+                              param_dtype="f32", keep=False)
+                t.append(time.perf_counter() - t0)
+        out["cpu_oracle_ms_per_step_1_thread"] = round(1e3 * float(np.median(t)), 3)
+    return out
 
 
 def adamw_times(gen, mo, dev, reps):
@@ -296,7 +311,7 @@ def main():
     # `value`); and the single 256x512 fp32 matrix, eager and replayed, where
     # launch latency dominates
     graph_ms = time_graph(opt, grads, args.steps) if ms.beta_ema < 0 or opt.ema_count > 0 else None
-    c1 = single_matrix_times(gen, mo, dev, args.steps)
+    c1 = single_matrix_times(gen, mo, dev, args.steps, with_oracle=not args.no_cpu_baseline)
     adamw = adamw_times(gen, mo, dev, max(args.steps, 20))
 
     sym, dense = gen.ns_flops(shapes, ms.steps)
