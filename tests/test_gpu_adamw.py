@@ -174,3 +174,29 @@ def test_capture_is_refused():
     opt.step(g)                       # eager steps still work afterwards
     torch.cuda.synchronize()
     assert opt.step_count == 2
+
+
+def test_tensor_beyond_int32_elements():
+    """One bf16 tensor of 2^31 + 4099 elements (64-bit element indices, a
+    ragged last chunk): moments bit for bit and parameters within tolerance
+    on sampled elements, including the last ones."""
+    announce("adamw 2^31 + 4099 elements")
+    n = 2 ** 31 + 4099
+    dev = torch.device("cuda")
+    gtr = torch.Generator(device=dev)
+    gtr.manual_seed(31)
+    p = torch.randn(n, generator=gtr, device=dev, dtype=torch.float32).mul_(0.5).to(torch.bfloat16)
+    g = torch.randn(n, generator=gtr, device=dev, dtype=torch.float32).mul_(1e-3).to(torch.bfloat16)
+    opt = mo.AdamW([p], lr=1e-2, betas=(0.9, 0.95), eps=1e-8, wd=0.1)
+    idx = torch.cat([torch.randint(0, n, (20000,), generator=gtr, device=dev),
+                     torch.arange(n - 5000, n, device=dev),
+                     torch.arange(2 ** 31 - 64, 2 ** 31 + 64, device=dev)])
+    p0 = host(p[idx]).astype(np.float64)
+    gs = host(g[idx])
+    opt.step([g])
+    torch.cuda.synchronize()
+    m_o, v_o = ada.adamw_moments_f32(np.zeros(len(gs), np.float32), np.zeros(len(gs), np.float32),
+                                     gs, HP[1], HP[2])
+    np.testing.assert_array_equal(host(opt.m[0][idx]), m_o)
+    np.testing.assert_array_equal(host(opt.v[0][idx]), v_o)
+    _check_params(p[idx], p0, m_o, v_o, 1, HP, torch.bfloat16, "p")

@@ -59,8 +59,10 @@ def test_single_matrix_256x512(kind, ns, tol):
     assert sigma_dev(O, ref) <= TOL_SIGMA
 
 
+# ten effective shapes: more than one grouped launch set per phase (at most
+# eight groups per launch)
 RAGGED = [(200, 333), (333, 200), (7, 11), (11, 7), (1, 5), (5, 1), (300, 300), (64, 1000),
-          (1000, 70), (200, 333), (129, 65)]
+          (1000, 70), (200, 333), (129, 65), (40, 90), (91, 41), (17, 257)]
 
 
 @pytest.mark.parametrize("tile", [64, 128, 256], indirect=True)
