@@ -148,13 +148,20 @@ __device__ __forceinline__ void storef16(float* row, bool vec, int valid, float*
   store16(row, kF32, vec, valid, v);
 }
 
+// Vector types that the nontemporal load/store builtins accept.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // 8 contiguous values of a row of bf16 or fp32 data (one 16-byte or two
 // 16-byte accesses when `vec`: the row start and every 8-element group are
-// 16-byte aligned).
+// 16-byte aligned).  NT marks the vector accesses nontemporal (data that is
+// streamed once).
+template <bool NT = false>
 __device__ __forceinline__ void load8(const void* row, int dt, bool vec, int valid, float* v) {
   if (vec && valid >= 8) {
     if (dt == kBF16) {
-      const uint4 q = *glb(reinterpret_cast<const uint4*>(row));
+      const GAS u32x4* pq = glb(reinterpret_cast<const u32x4*>(row));
+      const u32x4 q = NT ? __builtin_nontemporal_load(pq) : *pq;
       const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -162,8 +169,9 @@ __device__ __forceinline__ void load8(const void* row, int dt, bool vec, int val
         v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
       }
     } else {
-      const float4* p = glb(reinterpret_cast<const float4*>(row));
-      const float4 a = p[0], b = p[1];
+      const GAS f32x4* p = glb(reinterpret_cast<const f32x4*>(row));
+      const f32x4 a = NT ? __builtin_nontemporal_load(p) : p[0];
+      const f32x4 b = NT ? __builtin_nontemporal_load(p + 1) : p[1];
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
@@ -179,19 +187,23 @@ __device__ __forceinline__ void load8(const void* row, int dt, bool vec, int val
   }
 }
 
-// Store 8 values to a row of bf16 (RNE) or fp32 data; v returns the stored values.
+// Store 8 values to a row of bf16 (RNE) or fp32 data; v returns the stored
+// values.  NT as in load8.
+template <bool NT = false>
 __device__ __forceinline__ void store8(void* row, int dt, bool vec, int valid, float* v) {
   if (dt == kBF16) {
     uint16_t h[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) { h[k] = f2bf(v[k]); v[k] = bf2f(h[k]); }
     if (vec && valid >= 8) {
-      uint4 q;
+      u32x4 q;
       q.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
       q.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
       q.z = static_cast<uint32_t>(h[4]) | (static_cast<uint32_t>(h[5]) << 16);
       q.w = static_cast<uint32_t>(h[6]) | (static_cast<uint32_t>(h[7]) << 16);
-      *glb(reinterpret_cast<uint4*>(row)) = q;
+      GAS u32x4* pq = glb(reinterpret_cast<u32x4*>(row));
+      if (NT) __builtin_nontemporal_store(q, pq);
+      else *pq = q;
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -199,9 +211,15 @@ __device__ __forceinline__ void store8(void* row, int dt, bool vec, int valid, f
     }
   } else {
     if (vec && valid >= 8) {
-      float4* p = glb(reinterpret_cast<float4*>(row));
-      p[0] = make_float4(v[0], v[1], v[2], v[3]);
-      p[1] = make_float4(v[4], v[5], v[6], v[7]);
+      GAS f32x4* p = glb(reinterpret_cast<f32x4*>(row));
+      const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+      if (NT) {
+        __builtin_nontemporal_store(a, p);
+        __builtin_nontemporal_store(b, p + 1);
+      } else {
+        p[0] = a;
+        p[1] = b;
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -311,16 +329,19 @@ __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d
     valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
   }
   constexpr bool upd = STEP;
+  // the plain update streams O and W once: nontemporal accesses there
+  // (measured faster; slower with the extra state streams)
+  constexpr bool kNt = STEP && !CAUT && !EMA;
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
     if (valid[ps] <= 0) continue;
     // X rows sr < mp and columns sc .. sc+7 < np: in bounds
-    load8(static_cast<const char*>(xb) + (static_cast<int64_t>(sr[ps]) * d.np + sc) * esz, a.xdt,
-          true, 8, o[ps]);
+    load8<kNt>(static_cast<const char*>(xb) + (static_cast<int64_t>(sr[ps]) * d.np + sc) * esz,
+               a.xdt, true, 8, o[ps]);
     if (upd) {
       const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
-      load8(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
-            d.wdt, d.wvec, valid[ps], w[ps]);
+      load8<kNt>(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
+                 d.wdt, d.wvec, valid[ps], w[ps]);
       if (CAUT) load8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
       if (EMA && !a.ema_first) load8(d.ema + di, kF32, d.dvec, valid[ps], e[ps]);
     }
@@ -351,7 +372,7 @@ __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d
       const float dk = mk[k] != 0.f ? a.lrwd : 0.f;
       w[ps][k] = (w[ps][k] - dk * w[ps][k]) - a.lr * o[ps][k];
     }
-    store8(wrow, d.wdt, d.wvec, valid[ps], w[ps]);   // w now holds the stored values
+    store8<kNt>(wrow, d.wdt, d.wvec, valid[ps], w[ps]);   // w now holds the stored values
     if (EMA) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -506,6 +527,7 @@ __global__ __launch_bounds__(NT) void k_finish(ElemArgs a) {
   const int wsz = d.wdt == kBF16 ? 2 : 4;
   const void* xb = a.final_buf ? d.x1 : d.x0;
   const int sc = fj * kEw + lc;
+  constexpr bool kNt = STEP && !CAUT && !EMA;   // as in finish_strip
   int sr[NP], valid[NP];
   float x[NP][8], w[NP][8], sl[NP][8], e[NP][8];
 #pragma unroll
@@ -514,15 +536,15 @@ __global__ __launch_bounds__(NT) void k_finish(ElemArgs a) {
     valid[ps] = sr[ps] < d.rows ? max(0, min(8, d.cols - sc)) : 0;
     // X rows fj*64 + lr (+32) < mp, columns fi*64 + lc .. < np: in bounds
     const int64_t xi = static_cast<int64_t>(fj * kEw + lr + RPP * ps) * d.np + fi * kEw + lc;
-    load8(static_cast<const char*>(xb) + xi * esz, a.xdt, true, 8, x[ps]);
+    load8<kNt>(static_cast<const char*>(xb) + xi * esz, a.xdt, true, 8, x[ps]);
   }
   if (STEP) {
 #pragma unroll
     for (int ps = 0; ps < NP; ++ps) {
       if (valid[ps] <= 0) continue;
       const int64_t di = static_cast<int64_t>(sr[ps]) * d.cols + sc;
-      load8(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
-            d.wdt, d.wvec, valid[ps], w[ps]);
+      load8<kNt>(static_cast<const char*>(d.w) + (static_cast<int64_t>(sr[ps]) * d.ldw + sc) * wsz,
+                 d.wdt, d.wvec, valid[ps], w[ps]);
       if (CAUT) load8(d.slow + di, kF32, d.dvec, valid[ps], sl[ps]);
       if (EMA && !a.ema_first) load8(d.ema + di, kF32, d.dvec, valid[ps], e[ps]);
     }
@@ -563,7 +585,7 @@ __global__ __launch_bounds__(NT) void k_finish(ElemArgs a) {
       const float dk = mk[k] != 0.f ? a.lrwd : 0.f;
       w[ps][k] = (w[ps][k] - dk * w[ps][k]) - a.lr * o[ps][k];
     }
-    store8(wrow, d.wdt, d.wvec, valid[ps], w[ps]);   // w now holds the stored values
+    store8<kNt>(wrow, d.wdt, d.wvec, valid[ps], w[ps]);   // w now holds the stored values
     if (EMA) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -625,15 +647,16 @@ __global__ __launch_bounds__(NT) void k_adamw(AdamArgs a) {
   int64_t e0[NH];
   int valid[NH];
   float p[NH][8], g[NH][8], m[NH][8], v[NH][8];
+  // every element is read and written once: nontemporal accesses
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     e0[h] = base + h * (kAdamChunk / NH) + t * 8;
     valid[h] = static_cast<int>(max(int64_t(0), min(int64_t(8), d.n - e0[h])));
     if (valid[h] <= 0) continue;
-    load8(static_cast<const char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
-    load8(static_cast<const char*>(d.g) + e0[h] * gsz, d.gdt, d.gvec, valid[h], g[h]);
-    load8(d.m + e0[h], kF32, d.svec, valid[h], m[h]);
-    load8(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
+    load8<true>(static_cast<const char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
+    load8<true>(static_cast<const char*>(d.g) + e0[h] * gsz, d.gdt, d.gvec, valid[h], g[h]);
+    load8<true>(d.m + e0[h], kF32, d.svec, valid[h], m[h]);
+    load8<true>(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -647,9 +670,9 @@ __global__ __launch_bounds__(NT) void k_adamw(AdamArgs a) {
       const float u = m[h][k] / den;
       p[h][k] = (p[h][k] - a.lrwd * p[h][k]) - a.step_size * u;
     }
-    store8(static_cast<char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
-    store8(d.m + e0[h], kF32, d.svec, valid[h], m[h]);
-    store8(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
+    store8<true>(static_cast<char*>(d.p) + e0[h] * psz, d.pdt, d.pvec, valid[h], p[h]);
+    store8<true>(d.m + e0[h], kF32, d.svec, valid[h], m[h]);
+    store8<true>(d.v + e0[h], kF32, d.svec, valid[h], v[h]);
   }
 }
 
