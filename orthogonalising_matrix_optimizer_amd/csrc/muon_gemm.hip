@@ -86,11 +86,16 @@ __device__ __forceinline__ int rm_off(int k, int p) {
   return k * RB + (((p / EPC) ^ ((4 * (k & 3)) & (CPR - 1))) << 4) + (p % EPC) * ES;
 }
 
+// fp32 -> bf16, round to nearest even: gfx950 converts a pair per
+// instruction (v_cvt_pk_bf16_f32); NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Four consecutive elements <-> floats.
@@ -105,8 +110,8 @@ __device__ __forceinline__ void unpack4(const float4 q, float* v) {
 }
 __device__ __forceinline__ void st4(uint16_t* p, const float* v) {
   uint2 q;
-  q.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
-  q.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+  q.x = pack_bf16(v[0], v[1]);
+  q.y = pack_bf16(v[2], v[3]);
   *reinterpret_cast<uint2*>(p) = q;
 }
 __device__ __forceinline__ void st4(float* p, const float* v) {
@@ -472,10 +477,8 @@ __device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_
       for (int rg = 0; rg < 4; ++rg) {
         const int p = wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
         uint2 v;
-        v.x = static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4])) |
-              (static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4 + 1])) << 16);
-        v.y = static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4 + 2])) |
-              (static_cast<uint32_t>(f2bf(mult * acc[i][j][rg * 4 + 3])) << 16);
+        v.x = pack_bf16(mult * acc[i][j][rg * 4], mult * acc[i][j][rg * 4 + 1]);
+        v.y = pack_bf16(mult * acc[i][j][rg * 4 + 2], mult * acc[i][j][rg * 4 + 3]);
         *reinterpret_cast<uint2*>(stg + q * 512 + (((p >> 2) ^ stg_sw(q)) << 3)) = v;
       }
     }
