@@ -349,7 +349,10 @@ def main():
         "kernel_ms": phase_ms,
         "elementwise_gbs": {
             "prepare": round(prep_b / (phase_ms["prepare"] * 1e-3) / 1e9, 1),
-            "finish": round(fin_b / (phase_ms["finish"] * 1e-3) / 1e9, 1)},
+            "finish": (round(fin_b / (phase_ms["finish"] * 1e-3) / 1e9, 1)
+                       if phase_ms["finish"] else None)},
+        # the plain update runs in the last APPLY launch's epilogue (no finish launch)
+        "update_in_last_apply": phase_ms["finish"] is None,
         "roofline": {"bound": "mfma", "kernel": "APPLY (X <- aX + BX, bf16 MFMA)",
                      "achieved": round(a_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,

@@ -160,7 +160,13 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n,
  * params: n matrices, updated in place (bf16 is rounded to nearest even).
  * grads:  n matrices with the same shapes (any element type).
  * coeffs: HOST array of steps*3 floats.  steps in [0, MUON_MAX_STEPS].
- * lr, wd finite; beta in [0,1).  n == 0 only advances the counters. */
+ * lr, wd finite; beta in [0,1).  n == 0 only advances the counters.
+ * The plain update (no cautious mask, no average, no update_out/mask_out)
+ * of bf16 parameters whose rows, cols and ld are multiples of 8 and whose
+ * base is 16-byte aligned runs in the epilogue of the last Newton-Schulz
+ * launch (256-wide bf16 tiles, last iteration with b or c nonzero) instead
+ * of a separate kernel; it rounds O to bf16 and applies the same fp32
+ * operations, so the result is the same bit for bit. */
 int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
               const float* coeffs, int32_t steps, float lr, float wd,
               float beta, void* stream);
@@ -235,7 +241,10 @@ int muon_probe_disarm(void);
 /* Kernel configuration chosen for a shape list: number of effective-shape
  * groups, Newton-Schulz tile size per group (in `tiles`, up to `cap`
  * entries), and launches per step for `steps` iterations with coefficient
- * table `coeffs` (host, may be NULL for quintic). Returns a status. */
+ * table `coeffs` (host, may be NULL for quintic): one prepare launch, the
+ * Newton-Schulz launches, and one finish launch unless the plain update runs
+ * inside the last APPLY launch (see muon_step; counted here for options
+ * without the average). Returns a status. */
 int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt,
                    int32_t steps, const float* coeffs, int32_t* n_groups,
                    int32_t* tiles, int32_t cap, int32_t* launches_per_step);

@@ -36,6 +36,7 @@ int esize(int dt) { return dt == MUON_BF16 ? 2 : 4; }
 // ---------------------------------------------------------------- planning
 struct GroupPlan {
   int m = 0, n = 0, mp = 0, np = 0;
+  int fin_base = 0;                 // first entry of the group in the fused-update table
   std::vector<int> mats;
   size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0, off_part = 0;
   int64_t x_elems = 0, a_elems = 0;
@@ -54,7 +55,7 @@ struct Plan {
   std::vector<int> launch_groups;   // groups in launch order: costliest tiles first
   std::vector<GroupPlan> groups;
   std::vector<int> mat_group, mat_slot;
-  size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, total = 0;
+  size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, off_fin = 0, total = 0;
   std::vector<int64_t> pprefix, fprefix;
   // every padded iterate is addressable by the GEMMs' 32-bit buffer offsets
   bool fits = true;
@@ -164,6 +165,13 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
   p.off_fprefix = off;
   off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
+  // fused update table: the parameter matrices in group order
+  p.off_fin = off;
+  off = align_up(off + sizeof(FinDesc) * size_t(n), kAlign);
+  {
+    int base = 0;
+    for (auto& g : p.groups) { g.fin_base = base; base += int(g.mats.size()); }
+  }
   // every padded dimension is a multiple of the tile edge and of two K steps
   // of the GEMM pipeline (128 elements), so the K loop runs in pairs
   const int pad = std::max(p.ts, 128);
@@ -381,15 +389,49 @@ void fill_desc(MatDesc& d, const Plan& p, int i, const muon_mat& src_shape, char
 
 void table_bytes(const Plan& p, const std::vector<MatDesc>& desc, std::vector<uint8_t>& out) {
   const int n = int(desc.size());
-  out.assign(p.off_fprefix + sizeof(int64_t) * size_t(n + 1), 0);
+  out.assign(p.off_fin + sizeof(FinDesc) * size_t(n), 0);
   std::memcpy(out.data() + p.off_desc, desc.data(), sizeof(MatDesc) * size_t(n));
   std::memcpy(out.data() + p.off_pprefix, p.pprefix.data(), sizeof(int64_t) * size_t(n + 1));
   std::memcpy(out.data() + p.off_fprefix, p.fprefix.data(), sizeof(int64_t) * size_t(n + 1));
+  // the fused-update table depends on the matrices only (not on the options
+  // of a call), so the table a capture compares against stays the same
+  for (int i = 0; i < n; ++i) {
+    FinDesc f;
+    std::memset(&f, 0, sizeof(f));
+    f.w = desc[i].w;
+    f.ldw = desc[i].ldw;
+    f.rows = desc[i].rows;
+    f.cols = desc[i].cols;
+    f.tall = desc[i].tall;
+    const GroupPlan& g = p.groups[p.mat_group[i]];
+    std::memcpy(out.data() + p.off_fin + sizeof(FinDesc) * size_t(g.fin_base + p.mat_slot[i]), &f,
+                sizeof(f));
+  }
+}
+
+// Whether a step's plain update (no cautious mask, no average, no diagnostic
+// outputs) runs in the epilogue of its last APPLY instead of the finish
+// kernel: every parameter matrix bf16 with shapes, row pitch and base fit for
+// 16-byte chunks of 8 elements, 256-wide bf16 tiles, and a last iteration
+// that keeps the staged epilogue (b or c nonzero).  coeffs NULL: quintic.
+bool update_fusable(const Plan& p, const muon_mat* params, int n, bool cautious, bool avg,
+                    bool diag, const float* coeffs, int steps) {
+  if (n <= 0 || steps <= 0 || p.xdt != MUON_BF16 || p.ts != 256 || p.waves != 8 || cautious ||
+      avg || diag)
+    return false;
+  if (coeffs && coeffs[3 * (steps - 1) + 1] == 0.f && coeffs[3 * (steps - 1) + 2] == 0.f)
+    return false;
+  for (int i = 0; i < n; ++i)
+    if (params[i].dtype != MUON_BF16 || params[i].rows % 8 || params[i].cols % 8 ||
+        params[i].ld % 8 || reinterpret_cast<uintptr_t>(params[i].ptr) % 16)
+      return false;
+  return true;
 }
 
 // Newton-Schulz iterations; returns the buffer index holding the result.
 hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float eps,
-                  hipStream_t s, int* final_buf) {
+                  hipStream_t s, int* final_buf, bool fin = false, float lr = 0.f,
+                  float lrwd = 0.f) {
   int cur = 0;
   for (int j = 0; j < steps; ++j) {
     const float a = coeffs[3 * j], b = coeffs[3 * j + 1], c = coeffs[3 * j + 2];
@@ -409,6 +451,10 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
         int64_t blocks = 0;
         ga.ngroups = int(g1 - g0);
         ga.order = p.order[phase];
+        // last APPLY of a fused step: update the parameters instead of storing X
+        ga.fin = fin && phase == 2 && j == steps - 1;
+        ga.lr = lr;
+        ga.lrwd = lrwd;
         for (size_t gi = g0; gi < g1; ++gi) {
           const GroupPlan& g = p.groups[p.launch_groups[gi]];
           GemmGroup& d = ga.g[gi - g0];
@@ -421,6 +467,7 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
           d.p_stride = g.npart;
           d.npartials = g.npart;
           d.block_base = int(blocks);
+          d.fin = reinterpret_cast<const FinDesc*>(ws + p.off_fin) + g.fin_base;
           if (phase == 0) {
             d.xin = xin; d.out = ws + g.off_a;
             d.in_stride = g.x_elems; d.out_stride = g.a_elems;
@@ -647,18 +694,24 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   ea.ema_first = ema_on && st->ema_count == 0;
   ea.scale_o = steps == 0;
 
+  const bool fused = update_fusable(p, params, n, o.cautious, ema_on,
+                                    st->mask_out || st->update_out, coeffs, steps);
+
   probe_begin(MUON_PHASE_PREPARE, s);
   hipError_t err = launch_prepare(ea, p.pprefix[n], s);
   probe_end(MUON_PHASE_PREPARE, s);
   if (err != hipSuccess) return MUON_E_HIP;
   int fb = 0;
-  if (run_ns(p, ws, coeffs, steps, o.eps, s, &fb) != hipSuccess) return MUON_E_HIP;
-  ea.final_buf = fb;
-  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
-  probe_begin(MUON_PHASE_FINISH, s);
-  err = launch_finish(ea, p.fprefix[n], s);
-  probe_end(MUON_PHASE_FINISH, s);
-  if (err != hipSuccess) return MUON_E_HIP;
+  if (run_ns(p, ws, coeffs, steps, o.eps, s, &fb, fused, ea.lr, ea.lrwd) != hipSuccess)
+    return MUON_E_HIP;
+  if (!fused) {
+    ea.final_buf = fb;
+    ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+    probe_begin(MUON_PHASE_FINISH, s);
+    err = launch_finish(ea, p.fprefix[n], s);
+    probe_end(MUON_PHASE_FINISH, s);
+    if (err != hipSuccess) return MUON_E_HIP;
+  }
   st->step += 1;
   if (ema_on) st->ema_count += 1;
   if (weighted) st->avg_weight_sum = avg_sum;
@@ -869,7 +922,11 @@ int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt, i
     for (int i = 0; i < std::min<int>(cap, int(p.groups.size())); ++i) tiles[i] = p.ts;
   if (launches_per_step) {
     const int sets = int((p.groups.size() + kMaxGroups - 1) / kMaxGroups);
-    int l = n > 0 ? 2 : 0;
+    // prepare and finish; the finish runs inside the last APPLY when the
+    // update is fused (decided here without averaging or diagnostics)
+    const bool fused = update_fusable(p, params, n, opt && opt->cautious,
+                                      opt && opt->beta_ema >= 0.f, false, coeffs, steps);
+    int l = n > 0 ? (fused ? 1 : 2) : 0;
     for (int j = 0; j < steps && n > 0; ++j) {
       const bool poly = !coeffs || coeffs[3 * j + 2] != 0.f;
       l += sets * (poly ? 3 : 2);

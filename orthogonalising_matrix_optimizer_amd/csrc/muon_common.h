@@ -69,6 +69,16 @@ struct ElemArgs {
   int32_t scale_o;         // steps == 0: O = s * X0
 };
 
+// A parameter matrix updated in the last APPLY's epilogue (plain update,
+// bf16 W): W <- (W - lrwd W) - lr O.
+struct FinDesc {
+  void* w;                // W, bf16, row-major, 16-byte aligned rows
+  int64_t ldw;            // elements between W rows (multiple of 8)
+  int32_t rows, cols;     // W's shape (multiples of 8)
+  int32_t tall;           // the iterate is W transposed
+  int32_t _pad;
+};
+
 // One effective-shape group inside a grouped GEMM launch.
 struct GemmGroup {
   const void* xin;        // GRAM: X; POLY: A; APPLY: X
@@ -84,6 +94,7 @@ struct GemmGroup {
   int32_t tiles;          // tiles per matrix
   int32_t block_base;     // first block of this group in the launch
   int32_t npartials;
+  const FinDesc* fin;     // fused update: one entry per matrix of the group
 };
 
 struct GemmArgs {
@@ -97,6 +108,9 @@ struct GemmArgs {
                           // bit 1: row-major APPLY tile order;
                           // bit 2: whole matrices dealt to XCDs (j on j mod 8);
                           // bit 3: APPLY tiles by column panel
+  int32_t fin;            // APPLY (256-wide bf16, beta != 0): update W instead of
+                          // storing the iterate (the group's fin table)
+  float lr, lrwd;         // fused update: lr and fl(lr * wd)
 };
 
 }  // namespace muon

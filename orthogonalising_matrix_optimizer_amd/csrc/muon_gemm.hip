@@ -520,6 +520,104 @@ __device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_
   }
 }
 
+// Last APPLY of a plain step: instead of storing the iterate, update the
+// parameter matrix W <- (W - lrwd W) - lr O, with O = bf16(mult * acc) (the
+// value the iterate would be stored as) and the fp32 operation order of the
+// separate finish kernel, so W is bit for bit what that kernel writes.  The
+// tile goes through the staging tile as in staged_store; W rows are the
+// iterate's rows (16-byte row reads), or for a tall W its columns (the
+// transposing reads of the mirror path).  Each lane loads all of its W
+// chunks before it reads the staging tile, so their latency overlaps.
+// Shapes are multiples of 8, so an 8-element chunk is wholly inside W or
+// wholly in the padding.
+template <int WGP, int WGQ>
+__device__ __forceinline__ void staged_finish(uint8_t* stg, const FinDesc& f, int tP, int tQ,
+                                              float mult, float lr, float lrwd, int wave,
+                                              int lane, int wr, int wc,
+                                              f32x16_t (&acc)[256 / WGP / 32][256 / WGQ / 32]) {
+#pragma clang fp contract(off)
+  constexpr int TS = 256, NW = WGP * WGQ;
+  constexpr int WTP = TS / WGP, WTQ = TS / WGQ, FP = WTP / 32, FQ = WTQ / 32;
+  constexpr int NU = TS / (2 * NW);   // 16-byte chunks per lane
+  static_assert(NU == 128 / NW, "row and column passes move the same chunk count");
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < FP; ++i)
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int q = wc * WTQ + j * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int p = wr * WTP + i * 32 + rg * 8 + (lane >> 5) * 4;
+        uint2 v;
+        v.x = pack_bf16(mult * acc[i][j][rg * 4], mult * acc[i][j][rg * 4 + 1]);
+        v.y = pack_bf16(mult * acc[i][j][rg * 4 + 2], mult * acc[i][j][rg * 4 + 3]);
+        *reinterpret_cast<uint2*>(stg + q * 512 + (((p >> 2) ^ stg_sw(q)) << 3)) = v;
+      }
+    }
+  lds_barrier();
+  uint16_t* const w = static_cast<uint16_t*>(f.w);
+  const int g = lane >> 4, i = lane & 15;
+  const int goff = (g & 1) * 8 + (g >> 1);
+  int64_t off[NU];
+  bool ok[NU];
+  uint4 wv[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    int R, C;
+    if (!f.tall) {
+      const int q = 2 * (wave + NW * u) + (lane >> 5);
+      R = tQ * TS + q;
+      C = tP * TS + 8 * (lane & 31);
+    } else {
+      const int t = wave + NW * u;
+      const int n = t & 7, h = (t >> 3) & 3, m = t >> 5;
+      R = tP * TS + 4 * (16 * m + 2 * h + goff) + (i & 3);
+      C = tQ * TS + 32 * n + 8 * (i >> 2);
+    }
+    ok[u] = R < f.rows && C < f.cols;
+    off[u] = static_cast<int64_t>(R) * f.ldw + C;
+    if (ok[u]) wv[u] = *reinterpret_cast<const uint4*>(w + off[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    uint4 o;
+    if (!f.tall) {
+      const int q = 2 * (wave + NW * u) + (lane >> 5), c = lane & 31, sw = stg_sw(q);
+      o = *reinterpret_cast<const uint4*>(stg + q * 512 + ((c ^ (sw >> 1)) << 4));
+      if (sw & 1) o = make_uint4(o.z, o.w, o.x, o.y);
+    } else {
+      const int t = wave + NW * u;
+      const int n = t & 7, h = (t >> 3) & 3, m = t >> 5;
+      const int q0 = 32 * n, pq = 16 * m + 2 * h + goff;
+      i16x4_t r[2];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int q = q0 + 8 * (i & 3) + (i >> 2) + 4 * rr;
+        r[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(stg + q * 512 + ((pq ^ stg_sw(q)) << 3)));
+      }
+      o.x = static_cast<uint16_t>(r[0][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[0][1])) << 16);
+      o.y = static_cast<uint16_t>(r[0][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[0][3])) << 16);
+      o.z = static_cast<uint16_t>(r[1][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[1][1])) << 16);
+      o.w = static_cast<uint16_t>(r[1][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[1][3])) << 16);
+    }
+    if (!ok[u]) continue;
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+    const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+    uint32_t res[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o0 = __uint_as_float(ow[e] << 16), o1 = __uint_as_float(ow[e] & 0xffff0000u);
+      float w0 = __uint_as_float(ww[e] << 16), w1 = __uint_as_float(ww[e] & 0xffff0000u);
+      w0 = (w0 - lrwd * w0) - lr * o0;
+      w1 = (w1 - lrwd * w1) - lr * o1;
+      res[e] = pack_bf16(w0, w1);
+    }
+    *reinterpret_cast<uint4*>(w + off[u]) = make_uint4(res[0], res[1], res[2], res[3]);
+  }
+}
+
 // Logical block index: blocks are dealt round-robin to the eight XCDs; this
 // gives each XCD a contiguous range of logical tiles, so tiles that share
 // operand panels run on the same L2.
@@ -535,6 +633,8 @@ struct TileCoef {
   float cbb;          // APPLY: multiplier of the product (1, or b when B = bA)
   float eps;
   int first;          // first iteration: fold the norm scale s in
+  int fin;            // APPLY: update W in the epilogue (FinDesc of the matrix)
+  float lr, lrwd;
 };
 
 // One output tile (tP, tQ) of matrix `mat` of group G: K loop and epilogue.
@@ -635,6 +735,13 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   const int ld_out = MODE == APPLY ? G.np : G.mp;
   const float alpha = MODE == GRAM ? scale * scale : 1.f;
   const bool mirror = MODE != APPLY && tP != tQ;
+  if constexpr (kStaged && MODE == APPLY) {
+    if (capt && cf.fin) {
+      staged_finish<WGP, WGQ>(smem, G.fin[mat], tP, tQ, scale * cf.cbb, cf.lr, cf.lrwd, wave,
+                              lane, wr, wc, acc);
+      return;
+    }
+  }
   if constexpr (kStaged) {
     if (MODE == GRAM || capt) {
       const float mult = MODE == GRAM ? alpha : MODE == POLY ? cf.cc : scale * cf.cbb;
@@ -775,6 +882,7 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   TileCoef cf;
   cf.ca = args.ca; cf.cb = args.cb; cf.cc = args.cc; cf.cbb = args.cbb;
   cf.eps = args.eps; cf.first = args.first;
+  cf.fin = args.fin; cf.lr = args.lr; cf.lrwd = args.lrwd;
   gemm_tile<XDT, MODE, TS, WGP, WGQ>(G, mat, tP, tQ, cf, smem, red);
 }
 

@@ -266,10 +266,13 @@ def test_orthogonalize_and_blend_validation(lib):
 
 
 # ---------------------------------------------------------------- planning
-def _plan(lib, shapes, steps=5, coeffs=None, ns=_lib.MUON_BF16):
-    mats = _lib.mat_array((0, r, c, c, 0) for r, c in shapes)
+def _plan(lib, shapes, steps=5, coeffs=None, ns=_lib.MUON_BF16, cautious=0, beta_ema=-1.0,
+          pdt=_lib.MUON_BF16):
+    mats = _lib.mat_array((0, r, c, c, pdt) for r, c in shapes)
     opt = _lib.default_options()
     opt.ns_dtype = ns
+    opt.cautious = cautious
+    opt.beta_ema = beta_ema
     ng, lps = ctypes.c_int32(), ctypes.c_int32()
     tiles = (ctypes.c_int32 * 16)()
     c = _lib.float_array(np.array(coeffs if coeffs is not None else [gen.QUINTIC] * steps).ravel())
@@ -282,8 +285,16 @@ def test_plan_groups_and_launches(lib):
     shapes = gen.gpt124m_shapes()
     ng, ts, lps, ws = _plan(lib, shapes)
     assert ng == 2 and ts == 256
-    assert lps == 2 + 5 * 3                       # prepare, 5 x (gram, poly, apply), finish
-    assert _plan(lib, shapes, coeffs=[gen.CUBIC] * 5)[2] == 2 + 5 * 2
+    # prepare, 5 x (gram, poly, apply); the plain update of bf16 matrices with
+    # shapes in multiples of 8 runs in the last APPLY launch
+    assert lps == 1 + 5 * 3
+    assert _plan(lib, shapes, coeffs=[gen.CUBIC] * 5)[2] == 1 + 5 * 2
+    # a separate finish launch: cautious decay, the average, fp32 parameters, a
+    # shape that is not a multiple of 8
+    assert _plan(lib, shapes, cautious=1)[2] == 2 + 5 * 3
+    assert _plan(lib, shapes, beta_ema=0.99)[2] == 2 + 5 * 3
+    assert _plan(lib, shapes, pdt=_lib.MUON_F32)[2] == 2 + 5 * 3
+    assert _plan(lib, shapes + [(200, 333)])[2] == 2 + 5 * 3
     # iterate ping-pong + Gram + polynomial buffers for 48 (768,768) and 24 (768,3072)
     floor = 2 * (48 * (2 * 768 * 768 + 2 * 768 * 768) + 24 * (2 * 768 * 3072 + 2 * 768 * 768))
     assert floor <= ws <= floor * 1.01
