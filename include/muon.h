@@ -226,7 +226,9 @@ enum {
   MUON_PHASE_POLY = 2,     /* B = b A + c A^2                         */
   MUON_PHASE_APPLY = 3,    /* X <- a X + B X                          */
   MUON_PHASE_FINISH = 4,   /* update, mask, EMA (or write O)          */
-  MUON_PHASE_ADAMW = 5     /* the AdamW kernel of muon_adamw_step     */
+  MUON_PHASE_ADAMW = 5,    /* the AdamW kernel of muon_adamw_step     */
+  MUON_PHASE_APPLY_UPDATE = 6  /* last APPLY with the plain update of W
+                                  (see muon_step); not in MUON_PHASE_APPLY */
 };
 
 /* Record events around each of the next `capacity` launches of `phase`

@@ -17,7 +17,8 @@ STATUS = {
     11: "MUON_E_CAPTURE",
 }
 CODES = {v: k for k, v in STATUS.items()}
-PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4, "adamw": 5}
+PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4, "adamw": 5,
+          "apply_update": 6}
 MAX_STEPS = 16
 
 

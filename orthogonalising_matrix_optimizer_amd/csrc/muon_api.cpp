@@ -484,7 +484,8 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
           blocks += int64_t(d.count) * d.tiles;
         }
         (void)es;
-        const int ph = phase == 0 ? MUON_PHASE_GRAM : phase == 1 ? MUON_PHASE_POLY : MUON_PHASE_APPLY;
+        const int ph = phase == 0 ? MUON_PHASE_GRAM : phase == 1 ? MUON_PHASE_POLY
+                     : ga.fin ? MUON_PHASE_APPLY_UPDATE : MUON_PHASE_APPLY;
         probe_begin(ph, s);
         if (ga.order & 4) {
           // every XCD gets as many blocks as the one with the most matrices;
@@ -864,7 +865,7 @@ int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state
 }
 
 int muon_probe_arm(int32_t phase, int32_t capacity) {
-  if (phase < 0 || phase > MUON_PHASE_ADAMW || capacity < 1 || capacity > 65536)
+  if (phase < 0 || phase > MUON_PHASE_APPLY_UPDATE || capacity < 1 || capacity > 65536)
     return MUON_E_HPARAM;
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto e : g_probe.ev0) (void)hipEventDestroy(e);

@@ -633,13 +633,13 @@ struct TileCoef {
   float cbb;          // APPLY: multiplier of the product (1, or b when B = bA)
   float eps;
   int first;          // first iteration: fold the norm scale s in
-  int fin;            // APPLY: update W in the epilogue (FinDesc of the matrix)
-  float lr, lrwd;
+  float lr, lrwd;     // FIN: the update's lr and fl(lr * wd)
 };
 
 // One output tile (tP, tQ) of matrix `mat` of group G: K loop and epilogue.
-// smem holds NST * 2 * OPB bytes, red NW floats.
-template <int XDT, int MODE, int TS, int WGP, int WGQ>
+// smem holds NST * 2 * OPB bytes, red NW floats.  FIN (APPLY, 256-wide bf16,
+// beta != 0): update the matrix's W (G.fin) instead of storing the iterate.
+template <int XDT, int MODE, int TS, int WGP, int WGQ, bool FIN>
 __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, int tQ,
                                           const TileCoef& cf, uint8_t* smem, float* red) {
   using T = typename Ty<XDT>::T;
@@ -735,12 +735,11 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   const int ld_out = MODE == APPLY ? G.np : G.mp;
   const float alpha = MODE == GRAM ? scale * scale : 1.f;
   const bool mirror = MODE != APPLY && tP != tQ;
-  if constexpr (kStaged && MODE == APPLY) {
-    if (capt && cf.fin) {
-      staged_finish<WGP, WGQ>(smem, G.fin[mat], tP, tQ, scale * cf.cbb, cf.lr, cf.lrwd, wave,
-                              lane, wr, wc, acc);
-      return;
-    }
+  if constexpr (FIN) {
+    static_assert(kStaged && MODE == APPLY, "the update runs in the staged APPLY epilogue");
+    staged_finish<WGP, WGQ>(smem, G.fin[mat], tP, tQ, scale * cf.cbb, cf.lr, cf.lrwd, wave, lane,
+                            wr, wc, acc);
+    return;
   }
   if constexpr (kStaged) {
     if (MODE == GRAM || capt) {
@@ -807,7 +806,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
 }
 
 
-template <int XDT, int MODE, int TS, int WGP, int WGQ>
+template <int XDT, int MODE, int TS, int WGP, int WGQ, bool FIN>
 __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   constexpr int CPR = Ty<XDT>::CPR, NST = Ty<XDT>::NST;
   constexpr int NW = WGP * WGQ;       // waves per block
@@ -882,8 +881,8 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   TileCoef cf;
   cf.ca = args.ca; cf.cb = args.cb; cf.cc = args.cc; cf.cbb = args.cbb;
   cf.eps = args.eps; cf.first = args.first;
-  cf.fin = args.fin; cf.lr = args.lr; cf.lrwd = args.lrwd;
-  gemm_tile<XDT, MODE, TS, WGP, WGQ>(G, mat, tP, tQ, cf, smem, red);
+  cf.lr = args.lr; cf.lrwd = args.lrwd;
+  gemm_tile<XDT, MODE, TS, WGP, WGQ, FIN>(G, mat, tP, tQ, cf, smem, red);
 }
 
 template <int XDT, int MODE>
@@ -891,14 +890,22 @@ hipError_t launch_ts(int ts, int waves, const GemmArgs& a, int64_t blocks, hipSt
   const dim3 grid(static_cast<uint32_t>(blocks));
   if constexpr (XDT == kBF16) {
     if (ts == 256 && waves == 8) {
-      hipLaunchKernelGGL((k_gemm<XDT, MODE, 256, 2, 4>), grid, dim3(512), 0, s, a);
+      if constexpr (MODE == APPLY) {
+        if (a.fin) {
+          if (a.cbb == 0.f) return hipErrorInvalidValue;   // needs the staged epilogue
+          hipLaunchKernelGGL((k_gemm<XDT, MODE, 256, 2, 4, true>), grid, dim3(512), 0, s, a);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((k_gemm<XDT, MODE, 256, 2, 4, false>), grid, dim3(512), 0, s, a);
       return hipGetLastError();
     }
   }
+  if (a.fin) return hipErrorInvalidValue;
   if (ts == 128 && waves == 4)
-    hipLaunchKernelGGL((k_gemm<XDT, MODE, 128, 2, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<XDT, MODE, 128, 2, 2, false>), grid, dim3(256), 0, s, a);
   else if (ts == 64 && waves == 4)
-    hipLaunchKernelGGL((k_gemm<XDT, MODE, 64, 2, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<XDT, MODE, 64, 2, 2, false>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

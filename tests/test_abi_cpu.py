@@ -262,6 +262,11 @@ def test_orthogonalize_and_blend_validation(lib):
     assert lib.muon_ema_blend(p, p, st, 0.35, None) == E["MUON_E_STATE"]
     assert lib.muon_ema_blend(p, p, st, 1.5, None) == E["MUON_E_HPARAM"]
     assert lib.muon_probe_arm(9, 4) == E["MUON_E_HPARAM"]
+    assert lib.muon_probe_arm(7, 4) == E["MUON_E_HPARAM"]
+    # phase 6 (the APPLY launch that carries the update) is a phase; arming it
+    # creates HIP events, which fails without a GPU
+    assert lib.muon_probe_arm(6, 4) != E["MUON_E_HPARAM"]
+    lib.muon_probe_disarm()
     assert lib.muon_probe_arm(1, 0) == E["MUON_E_HPARAM"]
 
 

@@ -37,14 +37,17 @@ def _inputs(shapes, seed):
     return ws, grads
 
 
-def _step_count_finish(opt, grads):
-    """Take one step; return how many finish launches it made."""
-    mo.probe_arm("finish", 4)
+def _step_count(opt, grads, phase="finish"):
+    """Take one step; return how many launches of `phase` it made."""
+    mo.probe_arm(phase, 16)
     opt.step(grads)
     torch.cuda.synchronize()
-    n = len(mo.probe_read(4))
+    n = len(mo.probe_read(16))
     mo.probe_disarm()
     return n
+
+
+_step_count_finish = _step_count
 
 
 @pytest.mark.parametrize("coeffs,steps,wd", [("quintic", 5, 0.1), ("cubic", 5, 0.0),
@@ -136,3 +139,15 @@ def test_graph_replays_of_a_fused_step():
         torch.cuda.synchronize()
         for i in range(len(pa)):
             np.testing.assert_array_equal(host(pb[i]), host(pa[i]), err_msg=f"replay {t} W[{i}]")
+
+
+def test_launch_phases_of_a_fused_step():
+    """Five iterations: a fused step has four plain APPLY launches and one that
+    carries the update; an unfused step has five and a finish launch."""
+    announce("fused update: launch phases")
+    ws, grads = _inputs(SHAPES[:2], 12)
+    a = mo.Muon([dev_bf16(w) for w in ws], lr=0.02, diagnostics=True)
+    b = mo.Muon([dev_bf16(w) for w in ws], lr=0.02)
+    g = grads(0)
+    assert (_step_count(a, g, "apply"), _step_count(a, g, "apply_update")) == (5, 0)
+    assert (_step_count(b, g, "apply"), _step_count(b, g, "apply_update")) == (4, 1)
