@@ -151,3 +151,25 @@ def test_launch_phases_of_a_fused_step():
     g = grads(0)
     assert (_step_count(a, g, "apply"), _step_count(a, g, "apply_update")) == (5, 0)
     assert (_step_count(b, g, "apply"), _step_count(b, g, "apply_update")) == (4, 1)
+
+
+def test_nan_gradient_stays_in_its_matrix():
+    """A NaN in one gradient reaches only that matrix's parameters, as with the
+    finish kernel (NaN compares equal to NaN here)."""
+    announce("fused update: NaN confinement")
+    ws, grads = _inputs(SHAPES[:4], 13)
+    pa = [dev_bf16(w) for w in ws]
+    pb = [dev_bf16(w) for w in ws]
+    a = mo.Muon(pa, lr=0.02, wd=0.1, diagnostics=True)
+    b = mo.Muon(pb, lr=0.02, wd=0.1)
+    g = grads(0)
+    g[2][5, 7] = float("nan")
+    assert _step_count(a, g) == 1
+    assert _step_count(b, g) == 0
+    for i in range(len(pa)):
+        wa, wb = host(pa[i]), host(pb[i])
+        np.testing.assert_array_equal(wb, wa)
+        if i == 2:
+            assert np.isnan(wb).all()
+        else:
+            assert np.isfinite(wb).all()
