@@ -145,3 +145,34 @@ def test_large_sets_one_step_sampled(name, sample):
         assert bool(torch.isfinite(o).all())
         fro2 = float(o.double().square().sum())
         assert 0.0 < fro2 <= min(s) * (1 + 2 * TOL_BF16), (i, s, fro2 / min(s))
+
+
+@pytest.mark.parametrize("name", ["gpt124m", "gpt2p7b", "moe_share"])
+def test_bench_configuration_matches_finish_kernel(name):
+    """The configuration the benchmark times: no diagnostic outputs, so the
+    plain update runs in the last APPLY launch.  Every parameter matrix must be
+    bit for bit what a twin with diagnostic outputs (separate finish kernel,
+    checked against the oracle above) writes."""
+    announce(f"full size: {name} bench configuration vs finish kernel")
+    ms = gen.SETS[name]
+    shapes = list(ms.shapes)
+    coeffs = gen.coeff_table(ms.coeffs, ms.steps)
+    dev = torch.device("cuda")
+    pa = [gen.torch_param_matrix(r, c, 0, i, dev, dtype=torch.bfloat16)
+          for i, (r, c) in enumerate(shapes)]
+    pb = [p.clone() for p in pa]
+    grads = [gen.torch_grad_matrix(r, c, 0, 0, i, dev, rms=1e-3, dtype=torch.bfloat16)
+             for i, (r, c) in enumerate(shapes)]
+    kw = dict(lr=ms.lr, wd=ms.wd, beta=ms.beta, steps=ms.steps, coeffs=coeffs)
+    a = mo.Muon(pa, diagnostics=True, **kw)
+    b = mo.Muon(pb, **kw)
+    for t in range(2):
+        a.step(grads)
+        mo.probe_arm("finish", 4)
+        b.step(grads)
+        torch.cuda.synchronize()
+        assert len(mo.probe_read(4)) == 0, "the benchmark configuration launched a finish kernel"
+        mo.probe_disarm()
+        for i in range(len(shapes)):
+            assert torch.equal(pb[i], pa[i]), (t, i, shapes[i])
+            assert torch.equal(b.mom[i], a.mom[i]), (t, i, shapes[i])
