@@ -453,6 +453,7 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
         ga.order = p.order[phase];
         // last APPLY of a fused step: update the parameters instead of storing X
         ga.fin = fin && phase == 2 && j == steps - 1;
+        ga.ablk = p.ts == 256 && p.xdt == MUON_BF16 && p.waves == 8;
         ga.lr = lr;
         ga.lrwd = lrwd;
         for (size_t gi = g0; gi < g1; ++gi) {

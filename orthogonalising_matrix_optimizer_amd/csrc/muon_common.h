@@ -111,6 +111,8 @@ struct GemmArgs {
   int32_t fin;            // APPLY (256-wide bf16, beta != 0): update W instead of
                           // storing the iterate (the group's fin table)
   float lr, lrwd;         // fused update: lr and fl(lr * wd)
+  int32_t ablk;           // 256-wide bf16 tiles: A and B stored tile-contiguous
+                          // (256 x 64 blocks, see blk_off in the GEMM source)
 };
 
 }  // namespace muon

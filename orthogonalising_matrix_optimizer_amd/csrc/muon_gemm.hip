@@ -201,6 +201,7 @@ __device__ __forceinline__ void lds_barrier() {
 // (fixed across stages) and the uniform byte offset of the tile's origin.
 struct OpLoad {
   u32x4_t rs;
+  uint32_t kstep;      // bytes from one stage of 64 contraction elements to the next
   uint32_t voff;
   uint32_t origin;     // bytes: first row of the tile (and first column for row-major X)
   uint32_t ld_bytes;
@@ -355,8 +356,8 @@ __device__ __forceinline__ void gemm_issue(const OpLoad& la, const OpLoad& lb, i
   constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, OPB = TS * CPR * 16;
   const uint32_t k0 = static_cast<uint32_t>(k) * BK;
   if constexpr (MODE == APPLY) load_rm<TS, ES, BK, NW>(la, k0, wave, dst);
-  else load_kc<TS, NW, CPR>(la, k0 * ES, wave, dst);
-  load_kc<TS, NW, CPR>(lb, k0 * ES, wave, dst + OPB);
+  else load_kc<TS, NW, CPR>(la, static_cast<uint32_t>(k) * la.kstep, wave, dst);
+  load_kc<TS, NW, CPR>(lb, static_cast<uint32_t>(k) * lb.kstep, wave, dst + OPB);
 }
 
 // One stage: wait for stage k, refill the buffer of stage k-1 with stage
@@ -459,10 +460,19 @@ __device__ __forceinline__ int stg_sw(int q) { return (2 * (q & 15)) ^ ((q >> 4)
 // 16-byte row stores, and for off-diagonal GRAM/POLY tiles the mirror image
 // from transposing LDS reads (each 16-lane group turns 16 rows x 4 columns
 // into 4 rows x 16 columns).
+// Element offset of (r, c) in an m x m matrix stored tile-contiguous: blocks
+// of 256 rows x 64 columns (32 KB of bf16, rows of 128 bytes), block
+// (c / 64) * nbr + r / 256 for nbr = m / 256 row panels.  A stage of a row
+// panel is then one contiguous block for the LDS-DMA loads.
+__device__ __forceinline__ int64_t blk_off(int r, int c, int nbr) {
+  return (static_cast<int64_t>((c >> 6) * nbr + (r >> 8)) << 14) + ((r & 255) << 6) + (c & 63);
+}
+
+// nbr > 0: `out` is tile-contiguous with nbr row panels (ld unused).
 template <int MODE, int WGP, int WGQ>
-__device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_t ld, int tP,
-                                             int tQ, bool mirror, float mult, int wave, int lane,
-                                             int wr, int wc,
+__device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_t ld, int nbr,
+                                             int tP, int tQ, bool mirror, float mult, int wave,
+                                             int lane, int wr, int wc,
                                              f32x16_t (&acc)[256 / WGP / 32][256 / WGQ / 32]) {
   constexpr int TS = 256, NW = WGP * WGQ;
   constexpr int WTP = TS / WGP, WTQ = TS / WGQ, FP = WTP / 32, FQ = WTQ / 32;
@@ -489,7 +499,9 @@ __device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_
     const int q = 2 * (wave + NW * u) + (lane >> 5), c = lane & 31, sw = stg_sw(q);
     uint4 v = *reinterpret_cast<const uint4*>(stg + q * 512 + ((c ^ (sw >> 1)) << 4));
     if (sw & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(tQ * TS + q) * ld + tP * TS + 8 * c) = v;
+    const int64_t o = nbr ? blk_off(tQ * TS + q, tP * TS + 8 * c, nbr)
+                          : static_cast<int64_t>(tQ * TS + q) * ld + tP * TS + 8 * c;
+    *reinterpret_cast<uint4*>(out + o) = v;
   }
   if (!mirror) return;
   // mirror: a pair of transposing reads gives lane j of group g eight
@@ -515,8 +527,9 @@ __device__ __forceinline__ void staged_store(uint8_t* stg, uint16_t* out, int64_
     v.y = static_cast<uint16_t>(r[0][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[0][3])) << 16);
     v.z = static_cast<uint16_t>(r[1][0]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[1][1])) << 16);
     v.w = static_cast<uint16_t>(r[1][2]) | (static_cast<uint32_t>(static_cast<uint16_t>(r[1][3])) << 16);
-    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(tP * TS + p) * ld + tQ * TS + q0 +
-                              8 * (i >> 2)) = v;
+    const int64_t o = nbr ? blk_off(tP * TS + p, tQ * TS + q0 + 8 * (i >> 2), nbr)
+                          : static_cast<int64_t>(tP * TS + p) * ld + tQ * TS + q0 + 8 * (i >> 2);
+    *reinterpret_cast<uint4*>(out + o) = v;
   }
 }
 
@@ -634,6 +647,7 @@ struct TileCoef {
   float eps;
   int first;          // first iteration: fold the norm scale s in
   float lr, lrwd;     // FIN: the update's lr and fl(lr * wd)
+  int ablk;           // A and B are stored tile-contiguous (256-wide bf16 tiles)
 };
 
 // One output tile (tP, tQ) of matrix `mat` of group G: K loop and epilogue.
@@ -660,6 +674,22 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wr = wave / WGQ, wc = wave % WGQ;
 
+  // A and B (m x m) are tile-contiguous for 256-wide bf16 tiles: a stage of a
+  // row panel (256 rows x 64 contraction elements) is one 32 KB block
+  constexpr bool kStagedT = XDT == kBF16 && TS == 256;
+  const bool blk = kStagedT && cf.ablk;
+  const uint32_t blk_step = static_cast<uint32_t>(G.mp / TS) * TS * BK * ES;
+  auto plan_m = [&](OpLoad& o, int panel) {   // row panel of A or B
+    if (blk) {
+      o.ld_bytes = BK * ES;
+      o.origin = static_cast<uint32_t>(panel) * TS * BK * ES;
+      o.kstep = blk_step;
+    } else {
+      o.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
+      o.origin = static_cast<uint32_t>(panel) * TS * o.ld_bytes;
+      o.kstep = BK * ES;
+    }
+  };
   OpLoad la, lb;
   int K;
   if (MODE == GRAM || MODE == POLY) {
@@ -668,9 +698,15 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
     const uint32_t bytes = static_cast<uint32_t>(G.mp) * ld * ES;
     la.rs = make_desc(xin, bytes);
     lb.rs = la.rs;
-    la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
-    la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
-    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+    if (MODE == GRAM) {
+      la.ld_bytes = lb.ld_bytes = static_cast<uint32_t>(ld) * ES;
+      la.origin = static_cast<uint32_t>(tP) * TS * la.ld_bytes;
+      lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+      la.kstep = lb.kstep = BK * ES;
+    } else {
+      plan_m(la, tP);
+      plan_m(lb, tQ);
+    }
     plan_kc<CPR>(la, lane, wave);
     plan_kc<CPR>(lb, lane, wave);
   } else {
@@ -678,11 +714,11 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
     la.rs = make_desc(xin, static_cast<uint32_t>(G.mp) * G.np * ES);
     la.ld_bytes = static_cast<uint32_t>(G.np) * ES;
     la.origin = static_cast<uint32_t>(tP) * TS * ES;
+    la.kstep = 0;
     plan_rm<TS, ES, NW>(la, lane, wave);
     const T* bm = static_cast<const T*>(G.bop) + static_cast<int64_t>(mat) * G.b_stride;
     lb.rs = make_desc(bm, static_cast<uint32_t>(G.mp) * G.mp * ES);
-    lb.ld_bytes = static_cast<uint32_t>(G.mp) * ES;
-    lb.origin = static_cast<uint32_t>(tQ) * TS * lb.ld_bytes;
+    plan_m(lb, tQ);
     plan_kc<CPR>(lb, lane, wave);
   }
 
@@ -744,7 +780,9 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   if constexpr (kStaged) {
     if (MODE == GRAM || capt) {
       const float mult = MODE == GRAM ? alpha : MODE == POLY ? cf.cc : scale * cf.cbb;
-      staged_store<MODE, WGP, WGQ>(smem, reinterpret_cast<uint16_t*>(out), ld_out, tP, tQ,
+      // GRAM and POLY outputs (A, B) tile-contiguous when the plan says so
+      const int nbr = (MODE != APPLY && blk) ? G.mp / TS : 0;
+      staged_store<MODE, WGP, WGQ>(smem, reinterpret_cast<uint16_t*>(out), ld_out, nbr, tP, tQ,
                                    mirror, mult, wave, lane, wr, wc, acc);
       return;
     }
@@ -882,6 +920,7 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   cf.ca = args.ca; cf.cb = args.cb; cf.cc = args.cc; cf.cbb = args.cbb;
   cf.eps = args.eps; cf.first = args.first;
   cf.lr = args.lr; cf.lrwd = args.lrwd;
+  cf.ablk = args.ablk;
   gemm_tile<XDT, MODE, TS, WGP, WGQ, FIN>(G, mat, tP, tQ, cf, smem, red);
 }
 
