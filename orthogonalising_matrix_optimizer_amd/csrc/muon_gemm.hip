@@ -350,22 +350,25 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sa, const uint8_t* s
 }
 
 // Issue the loads of stage k into buffer `dst` ([A | B]).
+// share: a diagonal GRAM/POLY tile, whose two operands are the same row
+// panel, loads it once (the B half of the buffer is not used).
 template <int XDT, int MODE, int TS, int NW>
 __device__ __forceinline__ void gemm_issue(const OpLoad& la, const OpLoad& lb, int k, int wave,
-                                           uint8_t* dst) {
+                                           uint8_t* dst, bool share) {
   constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, OPB = TS * CPR * 16;
   const uint32_t k0 = static_cast<uint32_t>(k) * BK;
   if constexpr (MODE == APPLY) load_rm<TS, ES, BK, NW>(la, k0, wave, dst);
   else load_kc<TS, NW, CPR>(la, static_cast<uint32_t>(k) * la.kstep, wave, dst);
-  load_kc<TS, NW, CPR>(lb, static_cast<uint32_t>(k) * lb.kstep, wave, dst + OPB);
+  if (!share) load_kc<TS, NW, CPR>(lb, static_cast<uint32_t>(k) * lb.kstep, wave, dst + OPB);
 }
 
 // One stage: wait for stage k, refill the buffer of stage k-1 with stage
-// k + NST - 1, multiply from stage k.
+// k + NST - 1, multiply from stage k.  share (two-stage ring only: its wait
+// does not count loads): both operands from the A half of the buffer.
 template <int XDT, int MODE, int TS, int WGP, int WGQ>
 __device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, int k, int nk,
                                           int wave, int lane, int wr, int wc, uint8_t* cur,
-                                          uint8_t* fill,
+                                          uint8_t* fill, bool share,
                                           f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
   constexpr int ES = Ty<XDT>::ES, BK = Ty<XDT>::BK, CPR = Ty<XDT>::CPR, NST = Ty<XDT>::NST;
   constexpr int NW = WGP * WGQ, OPB = TS * CPR * 16, RPI = 64 / CPR;
@@ -382,13 +385,14 @@ __device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, in
   // bare barrier: a fenced __syncthreads would also wait for the loads of the
   // stages still in flight
   lds_barrier();
-  if (k + NST - 1 < nk) gemm_issue<XDT, MODE, TS, NW>(la, lb, k + NST - 1, wave, fill);
+  if (k + NST - 1 < nk) gemm_issue<XDT, MODE, TS, NW>(la, lb, k + NST - 1, wave, fill, share);
   // GRAM: the wave in its MFMA run takes issue priority over the other wave
   // of its SIMD (measured: GRAM 2.5 % faster; neutral for POLY, APPLY)
   if constexpr (MODE == GRAM) __builtin_amdgcn_s_setprio(1);
-  gemm_compute<XDT, MODE, TS, WGP, WGQ, 0>(cur, cur + OPB, lane, wr, wc, acc);
+  const uint8_t* const bop = share ? cur : cur + OPB;
+  gemm_compute<XDT, MODE, TS, WGP, WGQ, 0>(cur, bop, lane, wr, wc, acc);
   if constexpr (XDT == kBF16)
-    gemm_compute<XDT, MODE, TS, WGP, WGQ, 1>(cur, cur + OPB, lane, wr, wc, acc);
+    gemm_compute<XDT, MODE, TS, WGP, WGQ, 1>(cur, bop, lane, wr, wc, acc);
   if constexpr (MODE == GRAM) __builtin_amdgcn_s_setprio(0);
 }
 
@@ -403,11 +407,12 @@ __device__ __forceinline__ void gemm_step(const OpLoad& la, const OpLoad& lb, in
 // mult = s beta (APPLY) and coef = b / c, mult = c (POLY).
 template <int MODE, int TS, int WGP, int WGQ>
 __device__ __forceinline__ void capture_input(int k, const uint8_t* stage, int lane, int wr,
-                                              int wc, int tP, int tQ, float coef,
+                                              int wc, int tP, int tQ, float coef, bool share,
                                               f32x16_t (&acc)[TS / WGP / 32][TS / WGQ / 32]) {
   constexpr int WTP = TS / WGP, WTQ = TS / WGQ, FP = WTP / 32, FQ = WTQ / 32;
   constexpr int BK = Ty<kBF16>::BK, OPB = TS * Ty<kBF16>::CPR * 16;
   const int k0 = k * BK;
+  const uint8_t* const bst = share ? stage : stage + OPB;   // POLY: the B operand's rows
   if constexpr (MODE == APPLY) {
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
@@ -438,7 +443,7 @@ __device__ __forceinline__ void capture_input(int k, const uint8_t* stage, int l
           for (int rg = 0; rg < 4; ++rg) {
             const int kk = p0 - k0 + rg * 8 + (lane >> 5) * 4;
             float x[4];
-            unpack4(*reinterpret_cast<const uint2*>(stage + OPB + kc_off<8>(row, kk >> 3) +
+            unpack4(*reinterpret_cast<const uint2*>(bst + kc_off<8>(row, kk >> 3) +
                                                     (kk & 7) * 2), x);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][rg * 4 + e] += coef * x[e];
@@ -744,26 +749,31 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   // multiple of the stage count and each trip below runs the buffers in order
   const int nk = K / BK;
   if constexpr (NST == 4) {
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1);
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0, false);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 1, wave, sm1, false);
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 2, wave, sm2, false);
 #pragma unroll 1
     for (int kt = 0; kt < nk; kt += 4) {
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm3, false, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, false, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 2, nk, wave, lane, wr, wc, sm2, sm1, false, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 3, nk, wave, lane, wr, wc, sm3, sm2, false, acc);
     }
   } else {
-    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0);
+    // a diagonal GRAM/POLY tile loads its one row panel once per stage
+    const bool share = MODE != APPLY && tP == tQ;
+    gemm_issue<XDT, MODE, TS, NW>(la, lb, 0, wave, sm0, share);
 #pragma unroll 1
     for (int kt = 0; kt < nk; kt += 2) {
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm1, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt, nk, wave, lane, wr, wc, sm0, sm1, share, acc);
       if constexpr (kStaged && MODE != GRAM)
-        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt, sm0, lane, wr, wc, tP, tQ, coef, acc);
-      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, acc);
+        if (capt)
+          capture_input<MODE, TS, WGP, WGQ>(kt, sm0, lane, wr, wc, tP, tQ, coef, share, acc);
+      gemm_step<XDT, MODE, TS, WGP, WGQ>(la, lb, kt + 1, nk, wave, lane, wr, wc, sm1, sm0, share,
+                                         acc);
       if constexpr (kStaged && MODE != GRAM)
-        if (capt) capture_input<MODE, TS, WGP, WGQ>(kt + 1, sm1, lane, wr, wc, tP, tQ, coef, acc);
+        if (capt)
+          capture_input<MODE, TS, WGP, WGQ>(kt + 1, sm1, lane, wr, wc, tP, tQ, coef, share, acc);
     }
   }
 
