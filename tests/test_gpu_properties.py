@@ -1,0 +1,117 @@
+"""Properties the orthogonalisation has in exact arithmetic, checked on the GPU
+path itself against closed forms rather than against the oracle's arithmetic:
+rank-1 and diagonal inputs map through the scalar polynomial map, the map
+commutes with transposition, and scaling the input by a power of two leaves
+the output unchanged (bit for bit with eps = 0: every step of the bf16 path
+scales exactly).  bf16 operands; 256-wide tiles and small tiles."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import orthogonalising_matrix_optimizer_amd as mo
+from oracle import muon_oracle as orc
+from tests.gpu_helpers import TOL_BF16, announce, dev_f32, host
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+K = 5
+QUINTIC = gen.coeff_table("quintic", K)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mo._lib.load()
+
+
+@pytest.fixture(params=[64, 256])
+def tile(request, monkeypatch):
+    monkeypatch.setenv("MUON_TILE", str(request.param))
+    return request.param
+
+
+def _ortho(mats, eps=1e-7):
+    ins = [dev_f32(u) for u in mats]
+    outs = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in ins]
+    mo.orthogonalize(ins, outs, coeffs=QUINTIC, steps=K, ns_dtype="bf16", eps=eps)
+    torch.cuda.synchronize()
+    return [host(o) for o in outs]
+
+
+def _bf16(x):
+    """Values representable in bf16, so the device's cast is exact."""
+    return gen.f32_from_bf16_bits(gen.bf16_bits_from_f32(np.asarray(x, np.float32)))
+
+
+SHAPES = [(768, 1280), (1280, 768), (200, 336), (336, 200)]
+
+
+def _short(rng, n):
+    """Values with two mantissa bits times a power of two: every product of two
+    of them is exact in bf16, so u v^T is exactly rank one on the device."""
+    m = rng.choice([1.0, 1.25, 1.5, 1.75], n)
+    return m * np.exp2(rng.integers(-3, 1, n)) * rng.choice([-1.0, 1.0], n)
+
+
+def test_rank_one_input(tile):
+    """u v^T has one singular value s = |u||v|: the output is
+    p_K(s / (s + eps)) u v^T / s."""
+    announce(f"property: rank one, tile {tile}")
+    rng = np.random.default_rng(3)
+    mats, refs = [], []
+    for r, c in SHAPES:
+        u, v = _short(rng, r), _short(rng, c) * 2.0 ** -10
+        g = np.outer(u, v)
+        assert np.array_equal(_bf16(g), g.astype(np.float32))
+        sig = float(np.linalg.norm(u) * np.linalg.norm(v))
+        refs.append(orc.ns_poly_scalar(sig / (sig + 1e-7), QUINTIC) * g / sig)
+        mats.append(g.astype(np.float32))
+    for o, ref, s in zip(_ortho(mats), refs, SHAPES):
+        assert orc.rel_fro(o, ref) <= TOL_BF16, s
+
+
+def test_diagonal_input(tile):
+    """diag(d) (padded with zero columns): the output is diagonal, with
+    p_K(|d_i| / (|d| + eps)) sign(d_i) on the diagonal and exact zeros elsewhere."""
+    announce(f"property: diagonal, tile {tile}")
+    rng = np.random.default_rng(4)
+    for r, c in SHAPES:
+        m = min(r, c)
+        d = _bf16(rng.uniform(0.5, 2.0, m) * rng.choice([-1.0, 1.0], m) * 1e-2)
+        g = np.zeros((r, c), np.float32)
+        g[np.arange(m), np.arange(m)] = d
+        (o,) = _ortho([g])
+        nrm = float(np.sqrt(np.sum(d.astype(np.float64) ** 2)))
+        want = np.array([math.copysign(orc.ns_poly_scalar(abs(float(x)) / (nrm + 1e-7), QUINTIC),
+                                       float(x)) for x in d])
+        diag = o[np.arange(m), np.arange(m)].astype(np.float64)
+        assert np.max(np.abs(diag - want) / np.abs(want)) <= TOL_BF16, (r, c)
+        off = o.copy()
+        off[np.arange(m), np.arange(m)] = 0.0
+        assert not off.any(), (r, c)
+
+
+def test_transpose_commutes(tile):
+    """O(G^T) = O(G)^T: the tall input is transposed into the same wide iterate;
+    only the grouping of the norm's partial sums differs (fp32 rounding of s)."""
+    announce(f"property: transpose, tile {tile}")
+    mats = [gen.grad_matrix(r, c, 6, 0, i).astype(np.float32) for i, (r, c) in enumerate(SHAPES)]
+    a = _ortho(mats)
+    b = _ortho([np.ascontiguousarray(m.T) for m in mats])
+    for x, y, s in zip(a, b, SHAPES):
+        assert orc.rel_fro(y.T, x) <= 1e-3, s
+
+
+def test_power_of_two_scale_is_exact(tile):
+    """With eps = 0, O(4 G) and O(G / 8) equal O(G) bit for bit."""
+    announce(f"property: power-of-two scaling, tile {tile}")
+    mats = [_bf16(gen.grad_matrix(r, c, 7, 0, i)) for i, (r, c) in enumerate(SHAPES)]
+    base = _ortho(mats, eps=0.0)
+    for f in (4.0, 0.125):
+        scaled = _ortho([m * np.float32(f) for m in mats], eps=0.0)
+        for x, y, s in zip(base, scaled, SHAPES):
+            np.testing.assert_array_equal(y, x, err_msg=f"scale {f} {s}")
