@@ -154,7 +154,8 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   std::vector<std::pair<std::pair<int, int>, int>> shapes;
   for (auto& g : p.groups) shapes.push_back({{g.m, g.n}, int(g.mats.size())});
   p.ts = choose_ts(shapes, xdt);
-  // 256-wide (bf16) tiles run eight waves, two per SIMD; smaller tiles four
+  // 256-wide (bf16) tiles: GRAM runs eight waves, POLY and APPLY sixteen (the
+  // launcher picks the layout per phase); smaller tiles four
   p.waves = p.ts == 256 ? 8 : 4;
 
   const int es = esize(xdt);
