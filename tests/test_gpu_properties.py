@@ -1,7 +1,8 @@
 """Properties the orthogonalisation has in exact arithmetic, checked on the GPU
 path itself against closed forms rather than against the oracle's arithmetic:
 rank-1 and diagonal inputs map through the scalar polynomial map, the map
-commutes with transposition, and scaling the input by a power of two leaves
+commutes with transposition and with orthogonal rotations on either side, and
+scaling the input by a power of two leaves
 the output unchanged (bit for bit with eps = 0: every step of the bf16 path
 scales exactly).  bf16 operands; 256-wide tiles and small tiles."""
 import math
@@ -104,6 +105,25 @@ def test_transpose_commutes(tile):
     b = _ortho([np.ascontiguousarray(m.T) for m in mats])
     for x, y, s in zip(a, b, SHAPES):
         assert orc.rel_fro(y.T, x) <= 1e-3, s
+
+
+def test_orthogonal_equivariance(tile):
+    """O(Q G R) = Q O(G) R for orthogonal Q and R: the map acts on singular
+    values only.  Both sides carry their own bf16 rounding, so the comparison
+    is to the bf16 tolerance."""
+    announce(f"property: orthogonal equivariance, tile {tile}")
+    rng = np.random.default_rng(5)
+    mats, rot, qs, rs = [], [], [], []
+    for i, (r, c) in enumerate(SHAPES):
+        g = gen.grad_matrix(r, c, 8, 0, i).astype(np.float64)
+        q = np.linalg.qr(rng.standard_normal((r, r)))[0]
+        w = np.linalg.qr(rng.standard_normal((c, c)))[0]
+        mats.append(g.astype(np.float32))
+        rot.append((q @ g @ w).astype(np.float32))
+        qs.append(q)
+        rs.append(w)
+    for o, orot, q, w, s in zip(_ortho(mats), _ortho(rot), qs, rs, SHAPES):
+        assert orc.rel_fro(orot, q @ o.astype(np.float64) @ w) <= TOL_BF16, s
 
 
 def test_power_of_two_scale_is_exact(tile):
