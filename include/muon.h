@@ -246,7 +246,14 @@ int muon_probe_disarm(void);
  * table `coeffs` (host, may be NULL for quintic): one prepare launch, the
  * Newton-Schulz launches, and one finish launch unless the plain update runs
  * inside the last APPLY launch (see muon_step; counted here for options
- * without the average). Returns a status. */
+ * without the average). Returns a status.
+ * Two environment variables, read when a shape list is first planned, override
+ * the plan for experiments and tests: MUON_TILE=64|128|256 forces the tile
+ * width (256 only for bf16 iterates), and MUON_GEMM_ORDER="g,p,a" sets the
+ * block-order bits of the GRAM, POLY and APPLY launches (1 plain, 2 row-major
+ * APPLY tiles, 4 whole matrices dealt to XCDs, 8 APPLY by column panel).
+ * Results do not depend on MUON_GEMM_ORDER; MUON_TILE changes the rounding of
+ * the bf16 path within its tolerance. */
 int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt,
                    int32_t steps, const float* coeffs, int32_t* n_groups,
                    int32_t* tiles, int32_t cap, int32_t* launches_per_step);
