@@ -222,6 +222,11 @@ def test_golden_hand_worked_state():
     W = np.array(g["W"])
     S = np.array(g["S"])
     np.testing.assert_array_equal(orc.cautious_mask(W, S), np.array(g["mask"]) > 0)
+    u = orc.nesterov_f32(m, np.array(g["g"], np.float32), g["beta"][0])
+    np.testing.assert_array_equal(u, np.array(g["nesterov_u"], np.float32))
+    args = (np.array(g["w0"]), np.array(g["o"]), g["lr"][0], g["wd"][0], np.array(g["upd_mask"]) > 0)
+    np.testing.assert_array_equal(orc.update_f32(*args), np.array(g["w1"], np.float32))
+    np.testing.assert_array_equal(orc.update_f64(*args), np.array(g["w1"]))
 
 
 # ------------------------------------------------------------ fp32 state order
@@ -258,6 +263,60 @@ def test_update_f32_matches_scalar_emulation():
         t = _f32(float(wi) - _f32(d * float(wi)))
         want.append(_f32(t - _f32(_f32(lr) * float(oi))))
     np.testing.assert_array_equal(orc.update_f32(w, o, lr, wd, mk), np.array(want, np.float32))
+
+
+def test_update_f32_within_fp32_rounding_of_the_exact_update():
+    # every operation of the fp32 order rounds once (relative 2^-24), so the
+    # result lies within a few fp32 units of the operands' scale of the exact
+    # value; a dropped or mis-scaled term would be off by lr*wd*|w| or lr*|o|
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal(4000) * 0.02).astype(np.float32)
+    o = (rng.standard_normal(4000) * 0.03).astype(np.float32)
+    mk = rng.random(4000) < 0.5
+    for lr, wd in ((0.02, 0.1), (0.02, 1.6), (0.003, 0.0)):
+        lr32, wd32 = _f32(lr), _f32(wd)
+        exact = orc.update_f64(w, o, lr32, wd32, mk)
+        got = orc.update_f32(w, o, lr32, wd32, mk).astype(np.float64)
+        scale = np.abs(w) + lr32 * wd32 * np.abs(w) + lr32 * np.abs(o)
+        assert np.all(np.abs(got - exact) <= 4 * 2.0 ** -24 * scale)
+        assert np.max(np.abs(got - exact) / scale) > 0      # the fp32 order does round
+
+
+def test_nesterov_constant_gradient_closed_form():
+    # with M_0 = 0 and a constant gradient, M_t = (1 - beta^t) G, so the
+    # look-ahead beta M_t + (1 - beta) G is (1 - beta^(t+1)) G
+    G = (np.random.default_rng(4).standard_normal((5, 6))).astype(np.float32)
+    M = np.zeros_like(G)
+    beta = 0.95
+    for t in range(1, 41):
+        M = orc.momentum_f32(M, G, beta)
+        U = orc.nesterov_f32(M, G, beta)
+        np.testing.assert_allclose(U, (1 - beta ** (t + 1)) * G.astype(np.float64),
+                                   rtol=2e-6 * (t + 1), atol=1e-7)
+
+
+def test_nesterov_step_orthogonalises_the_look_ahead():
+    # two steps with independent gradients: M_2 = beta (1-beta) G1 + (1-beta) G2,
+    # and the step orthogonalises beta M_2 + (1-beta) G2
+    #   = beta^2 (1-beta) G1 + (1 - beta^2) G2
+    # (not M_2 itself, whose G1:G2 mix is beta : 1 instead of beta^2 : (1+beta))
+    shape = (7, 11)
+    G1 = gen.grad_matrix(*shape, 3, 1, 0).astype(np.float32).astype(np.float64)
+    G2 = gen.grad_matrix(*shape, 3, 2, 0).astype(np.float32).astype(np.float64)
+    beta, c = 0.8, _table("quintic", 5)
+    for nesterov in (True, False):
+        st = orc.OracleState([shape])
+        W = [np.zeros(shape)]
+        orc.muon_step(W, [G1], st, c, 0.02, 0.0, beta, param_dtype="f64", nesterov=nesterov)
+        out = orc.muon_step(W, [G2], st, c, 0.02, 0.0, beta, param_dtype="f64", nesterov=nesterov)
+        U = (beta ** 2 * (1 - beta) * G1 + (1 - beta ** 2) * G2 if nesterov
+             else beta * (1 - beta) * G1 + (1 - beta) * G2)
+        other = (beta * (1 - beta) * G1 + (1 - beta) * G2 if nesterov
+                 else beta ** 2 * (1 - beta) * G1 + (1 - beta ** 2) * G2)
+        want = _closed_form(U, c, 1e-7)
+        # fp32 state rounding of M and U: relative ~1e-7
+        assert orc.rel_fro(out["O"][0], want) < 1e-5
+        assert orc.rel_fro(out["O"][0], _closed_form(other, c, 1e-7)) > 1e-2
 
 
 # -------------------------------------------------- recurrence closed forms
