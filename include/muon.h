@@ -166,7 +166,12 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n,
  * base is 16-byte aligned runs in the epilogue of the last Newton-Schulz
  * launch (256-wide bf16 tiles, last iteration with b or c nonzero) instead
  * of a separate kernel; it rounds O to bf16 and applies the same fp32
- * operations, so the result is the same bit for bit. */
+ * operations, so the result is the same bit for bit.
+ * The bf16 products fold the term b A (or a X) into the accumulators as
+ * (b/c) A (or (a/b) X) and scale at the store; a table with a row whose ratio
+ * is not finite, above 2^32 in magnitude, or whose divisor is below 2^-32
+ * runs every launch of the call with the term added at the store instead
+ * (same results within rounding, a little slower). */
 int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
               const float* coeffs, int32_t steps, float lr, float wd,
               float beta, void* stream);
@@ -176,26 +181,40 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
  * end-to-end gain).  Besides its kernel launches, muon_step enqueues one
  * host-to-device copy of a per-workspace descriptor table (matrix pointers,
  * shapes, tile offsets) from pinned staging memory, on every call; it does
- * not synchronise the stream.  Under capture no copy is made: the table must
- * already be in the workspace.  muon_step_prepare validates the arguments
- * exactly as muon_step does and sends that table for these
+ * not synchronise the stream.  The workspace holds two table regions (see
+ * muon_workspace_layout): uncaptured calls send and read the eager region;
+ * muon_step_prepare sends the capture region, and a call under capture makes
+ * no copy and reads the capture region.  muon_step_prepare validates the
+ * arguments exactly as muon_step does and sends that table for these
  * params/grads/state buffers, without launching anything or touching the
  * counters.  After it, a muon_step with the same buffers can be captured
  * (hipStreamBeginCapture, or a framework's graph capture) on `stream`; a
- * captured call whose table is not resident returns MUON_E_CAPTURE and
- * enqueues nothing.
+ * captured call whose table does not match the capture region returns
+ * MUON_E_CAPTURE and enqueues nothing.  Eager muon_step, muon_orthogonalize
+ * and muon_ema_blend calls on the same workspace between replays leave the
+ * capture region alone; another muon_step_prepare on the workspace replaces
+ * it (the earlier graph would then replay with the new table).
  * A replay repeats the captured step on the same buffers with the captured
  * scalars: lr, wd, beta, coefficients, options, the weight-average
  * coefficients, and the flags derived from the counters (whether this step is
  * averaged, and whether it is the first averaged step).  The capturing call
  * advances step/ema_count once as for an eager call; replays do not touch the
- * host state, so the caller advances the counters per replay and captures
- * only steps whose flags and coefficients repeat (weight average disabled, or
- * an exponential average already started).  A captured step that would fold
- * into a MUON_AVG_WEIGHTED average returns MUON_E_CAPTURE (its coefficients
- * change every step).  Same errors as muon_step. */
+ * host state: advance the counters with muon_state_advance per replay, and
+ * capture only steps whose flags and coefficients repeat (weight average
+ * disabled, or an exponential average already started).  A captured step that
+ * would fold into a MUON_AVG_WEIGHTED average returns MUON_E_CAPTURE (its
+ * coefficients change every step).  Same errors as muon_step. */
 int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state* st,
                       void* stream);
+
+/* Counter advance for replayed captured steps (see muon_step_prepare): adds
+ * `replays` steps to st->step and, when the weight average is on and the
+ * step has reached ema_start, as many to st->ema_count, exactly as that many
+ * eager calls would.  Errors: MUON_E_NULL; MUON_E_HPARAM (replays < 0 or bad
+ * options); MUON_E_CAPTURE when the state's average could not have been
+ * captured (a MUON_AVG_WEIGHTED average, or an exponential average that has
+ * not started yet), the counters then unchanged.  Touches no device memory. */
+int muon_state_advance(muon_state* st, int32_t replays);
 
 /* Newton-Schulz part alone: out[i] = orthogonalise(in[i]) for n matrices
  * (same shapes; out may be any element type; in and out must not overlap).
@@ -239,6 +258,17 @@ int muon_probe_arm(int32_t phase, int32_t capacity);
 int muon_probe_read(float* ms, int32_t capacity, int32_t* count);
 /* Stop recording and release the events. */
 int muon_probe_disarm(void);
+
+/* Workspace layout of muon_step for a shape list (byte offsets from the
+ * workspace base): the descriptor-table region that uncaptured calls send and
+ * read (muon_step, muon_orthogonalize, muon_ema_blend), the region that
+ * muon_step_prepare sends and captured steps read, the size of one region,
+ * and the first byte of the iterate and product buffers.  The two regions
+ * are disjoint, so no uncaptured call on the workspace changes the table a
+ * replay reads; only another muon_step_prepare on it does. */
+int muon_workspace_layout(const muon_mat* params, int32_t n, const muon_options* opt,
+                          size_t* eager_table, size_t* capture_table, size_t* table_bytes,
+                          size_t* buffers);
 
 /* Kernel configuration chosen for a shape list: number of effective-shape
  * groups, Newton-Schulz tile size per group (in `tiles`, up to `cap`

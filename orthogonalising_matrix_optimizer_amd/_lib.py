@@ -6,7 +6,9 @@ import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint8, c_void_p
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmuon_mi355x.so")
+# MUON_LIB_PATH selects another build of the same library (the host-sanitised
+# build of the C ABI used by the CPU tests); the default is the in-tree build
+LIB_PATH = os.environ.get("MUON_LIB_PATH") or os.path.join(PKG, "libmuon_mi355x.so")
 
 MUON_BF16, MUON_F32 = 0, 1
 MUON_AVG_EMA, MUON_AVG_WEIGHTED = 0, 1
@@ -103,6 +105,11 @@ def load() -> ctypes.CDLL:
     lib.muon_plan_info.argtypes = [P(MuonMat), c_int32, P(MuonOptions), c_int32, P(c_float),
                                    P(c_int32), P(c_int32), c_int32, P(c_int32)]
     lib.muon_plan_info.restype = c_int32
+    lib.muon_state_advance.argtypes = [P(MuonState), c_int32]
+    lib.muon_state_advance.restype = c_int32
+    lib.muon_workspace_layout.argtypes = [P(MuonMat), c_int32, P(MuonOptions), P(c_size_t),
+                                          P(c_size_t), P(c_size_t), P(c_size_t)]
+    lib.muon_workspace_layout.restype = c_int32
     lib.muon_adamw_workspace_bytes.argtypes = [c_int32]
     lib.muon_adamw_workspace_bytes.restype = c_size_t
     lib.muon_adamw_step.argtypes = [P(MuonVec), P(MuonVec), P(AdamWState), P(AdamWHparams),

@@ -28,6 +28,8 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kCUs = 256;
+// descriptor-table regions of the workspace
+constexpr int kTabEager = 0, kTabCapture = 1;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -55,7 +57,13 @@ struct Plan {
   std::vector<int> launch_groups;   // groups in launch order: costliest tiles first
   std::vector<GroupPlan> groups;
   std::vector<int> mat_group, mat_slot;
-  size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, off_fin = 0, total = 0;
+  // descriptor table: offsets inside one table region, and the regions
+  // themselves (kTabEager: sent by every uncaptured call; kTabCapture: sent by
+  // muon_step_prepare only and read by captured steps, so no eager call on the
+  // same workspace can change what a replay reads)
+  size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, off_fin = 0, tab_bytes = 0;
+  size_t off_tab[2] = {0, 0};
+  size_t total = 0;
   std::vector<int64_t> pprefix, fprefix;
   // every padded iterate is addressable by the GEMMs' 32-bit buffer offsets
   bool fits = true;
@@ -169,6 +177,10 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   // fused update table: the parameter matrices in group order
   p.off_fin = off;
   off = align_up(off + sizeof(FinDesc) * size_t(n), kAlign);
+  p.tab_bytes = off;
+  p.off_tab[kTabEager] = 0;
+  p.off_tab[kTabCapture] = p.tab_bytes;
+  off = 2 * p.tab_bytes;
   {
     int base = 0;
     for (auto& g : p.groups) { g.fin_base = base; base += int(g.mats.size()); }
@@ -415,10 +427,31 @@ void table_bytes(const Plan& p, const std::vector<MatDesc>& desc, std::vector<ui
 // kernel: every parameter matrix bf16 with shapes, row pitch and base fit for
 // 16-byte chunks of 8 elements, 256-wide bf16 tiles, and a last iteration
 // that keeps the staged epilogue (b or c nonzero).  coeffs NULL: quintic.
+// The staged epilogue of 256-wide bf16 tiles folds the input term into the
+// product during the K loop: POLY keeps acc = A A + (b/c) A and stores c acc,
+// a cubic APPLY keeps acc = A X + (a/b) X and stores s b acc.  A ratio or a
+// multiplier far from one could overflow the fp32 accumulators where the
+// unfolded sum is finite, so a coefficient table with such a row runs the
+// plain epilogue (input term added at the store, A and B row-major) in every
+// launch of the call.  The ratio is formed in fp32, as the kernels form it.
+bool fold_ok(float num, float den) {
+  const float r = num / den;
+  return std::isfinite(r) && std::fabs(r) <= 0x1p32f && std::fabs(den) >= 0x1p-32f;
+}
+
+bool folding_safe(const float* coeffs, int steps) {
+  if (!coeffs) return true;   // quintic
+  for (int j = 0; j < steps; ++j) {
+    const float a = coeffs[3 * j], b = coeffs[3 * j + 1], c = coeffs[3 * j + 2];
+    if (c != 0.f ? !fold_ok(b, c) : (b != 0.f && !fold_ok(a, b))) return false;
+  }
+  return true;
+}
+
 bool update_fusable(const Plan& p, const muon_mat* params, int n, bool cautious, bool avg,
                     bool diag, const float* coeffs, int steps) {
   if (n <= 0 || steps <= 0 || p.xdt != MUON_BF16 || p.ts != 256 || p.waves != 8 || cautious ||
-      avg || diag)
+      avg || diag || !folding_safe(coeffs, steps))
     return false;
   if (coeffs && coeffs[3 * (steps - 1) + 1] == 0.f && coeffs[3 * (steps - 1) + 2] == 0.f)
     return false;
@@ -430,10 +463,12 @@ bool update_fusable(const Plan& p, const muon_mat* params, int n, bool cautious,
 }
 
 // Newton-Schulz iterations; returns the buffer index holding the result.
-hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float eps,
-                  hipStream_t s, int* final_buf, bool fin = false, float lr = 0.f,
+// tab: the descriptor-table region the launches read.
+hipError_t run_ns(const Plan& p, char* ws, const char* tab, const float* coeffs, int steps,
+                  float eps, hipStream_t s, int* final_buf, bool fin = false, float lr = 0.f,
                   float lrwd = 0.f) {
   int cur = 0;
+  const bool fold = folding_safe(coeffs, steps);
   for (int j = 0; j < steps; ++j) {
     const float a = coeffs[3 * j], b = coeffs[3 * j + 1], c = coeffs[3 * j + 2];
     const bool poly = c != 0.f;
@@ -454,7 +489,8 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
         ga.order = p.order[phase];
         // last APPLY of a fused step: update the parameters instead of storing X
         ga.fin = fin && phase == 2 && j == steps - 1;
-        ga.ablk = p.ts == 256 && p.xdt == MUON_BF16 && p.waves == 8;
+        ga.ablk = fold && p.ts == 256 && p.xdt == MUON_BF16 && p.waves == 8;
+        ga.nofold = !fold;
         ga.lr = lr;
         ga.lrwd = lrwd;
         for (size_t gi = g0; gi < g1; ++gi) {
@@ -469,7 +505,7 @@ hipError_t run_ns(const Plan& p, char* ws, const float* coeffs, int steps, float
           d.p_stride = g.npart;
           d.npartials = g.npart;
           d.block_base = int(blocks);
-          d.fin = reinterpret_cast<const FinDesc*>(ws + p.off_fin) + g.fin_base;
+          d.fin = reinterpret_cast<const FinDesc*>(tab + p.off_fin) + g.fin_base;
           if (phase == 0) {
             d.xin = xin; d.out = ws + g.off_a;
             d.in_stride = g.x_elems; d.out_stride = g.a_elems;
@@ -623,17 +659,19 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
     rows[i] = params[i].rows;
     cols[i] = params[i].cols;
   }
-  if (!st->workspace) return MUON_E_WORKSPACE;
+  void* const wsp = st->workspace;
+  const size_t ws_bytes = st->workspace_bytes;
+  if (!wsp) return MUON_E_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_mu);
   const Plan& p = get_plan(rows.data(), cols.data(), n, o.ns_dtype);
   if (!p.fits) return MUON_E_SHAPE;
-  if (st->workspace_bytes < p.total) return MUON_E_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(st->workspace) % kAlign) return MUON_E_ALIGN;
-  add_range(ranges, st->workspace, p.total);
+  if (ws_bytes < p.total) return MUON_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(wsp) % kAlign) return MUON_E_ALIGN;
+  add_range(ranges, wsp, p.total);
   if (overlaps(ranges)) return MUON_E_ALIAS;
 
   // ---- descriptor table
-  char* ws = static_cast<char*>(st->workspace);
+  char* ws = static_cast<char*>(wsp);
   std::vector<MatDesc> desc(n);
   for (int i = 0; i < n; ++i) {
     MatDesc& d = desc[i];
@@ -657,20 +695,22 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (weighted && !prepare_only) {
-    // the weighted average's coefficients change with every step: a replayed
-    // capture would repeat stale ones
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MUON_E_HIP;
-    if (cs != hipStreamCaptureStatusNone) return MUON_E_CAPTURE;
-  }
-  if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MUON_E_HIP;
+  const bool capturing = cs != hipStreamCaptureStatusNone;
+  // the weighted average's coefficients change with every step: a replayed
+  // capture would repeat stale ones
+  if (weighted && capturing && !prepare_only) return MUON_E_CAPTURE;
+  // muon_step_prepare fills the capture region, which captured steps read;
+  // uncaptured steps send and read the eager region
+  const char* tab = ws + p.off_tab[(prepare_only || capturing) ? kTabCapture : kTabEager];
+  if ((rc = upload_table(const_cast<char*>(tab), bytes, s)) != MUON_OK) return rc;
   if (prepare_only) return MUON_OK;
 
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
-  ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
-  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_pprefix);
+  ea.mats = reinterpret_cast<const MatDesc*>(tab + p.off_desc);
+  ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_pprefix);
   ea.nmats = n;
   ea.xdt = p.xdt;
   ea.beta = beta;
@@ -705,11 +745,11 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   probe_end(MUON_PHASE_PREPARE, s);
   if (err != hipSuccess) return MUON_E_HIP;
   int fb = 0;
-  if (run_ns(p, ws, coeffs, steps, o.eps, s, &fb, fused, ea.lr, ea.lrwd) != hipSuccess)
+  if (run_ns(p, ws, tab, coeffs, steps, o.eps, s, &fb, fused, ea.lr, ea.lrwd) != hipSuccess)
     return MUON_E_HIP;
   if (!fused) {
     ea.final_buf = fb;
-    ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+    ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_fprefix);
     probe_begin(MUON_PHASE_FINISH, s);
     err = launch_finish(ea, p.fprefix[n], s);
     probe_end(MUON_PHASE_FINISH, s);
@@ -730,6 +770,52 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st, con
 int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state* st,
                       void* stream) {
   return step_impl(params, grads, st, nullptr, 0, 0.f, 0.f, 0.f, stream, true);
+}
+
+
+int muon_state_advance(muon_state* st, int32_t replays) {
+  if (!st) return MUON_E_NULL;
+  if (replays < 0) return MUON_E_HPARAM;
+  int rc;
+  if ((rc = check_opt(st->opt)) != MUON_OK) return rc;
+  const muon_options& o = st->opt;
+  // a replayed step repeats the captured weight-average flags: averaging must
+  // be off or an exponential average already started (the capture rules)
+  if (o.beta_ema >= 0.f) {
+    if (o.avg_mode != MUON_AVG_EMA) return MUON_E_CAPTURE;
+    if (st->ema_count == 0 || st->step + 1 < o.ema_start) return MUON_E_CAPTURE;
+  }
+  for (int32_t r = 0; r < replays; ++r) {
+    st->step += 1;
+    if (o.beta_ema >= 0.f && st->step >= o.ema_start) st->ema_count += 1;
+  }
+  return MUON_OK;
+}
+
+int muon_workspace_layout(const muon_mat* params, int32_t n, const muon_options* opt,
+                          size_t* eager_table, size_t* capture_table, size_t* table_bytes,
+                          size_t* buffers) {
+  if (n < 0) return MUON_E_SHAPE;
+  if ((n > 0 && !params) || !eager_table || !capture_table || !table_bytes || !buffers)
+    return MUON_E_NULL;
+  const int xdt = opt ? opt->ns_dtype : MUON_BF16;
+  if (xdt != MUON_BF16 && xdt != MUON_F32) return MUON_E_DTYPE;
+  std::vector<int64_t> rows(n), cols(n);
+  for (int i = 0; i < n; ++i) {
+    if (params[i].rows < 1 || params[i].cols < 1) return MUON_E_SHAPE;
+    if (params[i].rows > (int64_t(1) << 30) || params[i].cols > (int64_t(1) << 30))
+      return MUON_E_SHAPE;
+    rows[i] = params[i].rows;
+    cols[i] = params[i].cols;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  const Plan& p = get_plan(rows.data(), cols.data(), n, xdt);
+  if (!p.fits) return MUON_E_SHAPE;
+  *eager_table = p.off_tab[kTabEager];
+  *capture_table = p.off_tab[kTabCapture];
+  *table_bytes = p.tab_bytes;
+  *buffers = p.groups.empty() ? p.total : p.groups[0].off_x0;
+  return MUON_OK;
 }
 
 int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const float* coeffs,
@@ -782,11 +868,12 @@ int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
+  char* tab = ws + p.off_tab[kTabEager];
+  if ((rc = upload_table(tab, bytes, s)) != MUON_OK) return rc;
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
-  ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
-  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_pprefix);
+  ea.mats = reinterpret_cast<const MatDesc*>(tab + p.off_desc);
+  ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_pprefix);
   ea.nmats = n;
   ea.xdt = p.xdt;
   ea.eps = o.eps;
@@ -797,9 +884,9 @@ int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const
   probe_end(MUON_PHASE_PREPARE, s);
   if (err != hipSuccess) return MUON_E_HIP;
   int fb = 0;
-  if (run_ns(p, ws, coeffs, steps, o.eps, s, &fb) != hipSuccess) return MUON_E_HIP;
+  if (run_ns(p, ws, tab, coeffs, steps, o.eps, s, &fb) != hipSuccess) return MUON_E_HIP;
   ea.final_buf = fb;
-  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+  ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_fprefix);
   probe_begin(MUON_PHASE_FINISH, s);
   err = launch_finish(ea, p.fprefix[n], s);
   probe_end(MUON_PHASE_FINISH, s);
@@ -855,11 +942,14 @@ int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state
   std::vector<uint8_t> bytes;
   table_bytes(p, desc, bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = upload_table(ws, bytes, s)) != MUON_OK) return rc;
+  // the eager region: a captured step reads the capture region, which only
+  // muon_step_prepare writes
+  char* tab = ws + p.off_tab[kTabEager];
+  if ((rc = upload_table(tab, bytes, s)) != MUON_OK) return rc;
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
-  ea.mats = reinterpret_cast<const MatDesc*>(ws + p.off_desc);
-  ea.prefix = reinterpret_cast<const int64_t*>(ws + p.off_fprefix);
+  ea.mats = reinterpret_cast<const MatDesc*>(tab + p.off_desc);
+  ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_fprefix);
   ea.nmats = n;
   const float wf = w_final;
   volatile float owf = 1.0f - wf;

@@ -113,6 +113,9 @@ struct GemmArgs {
   float lr, lrwd;         // fused update: lr and fl(lr * wd)
   int32_t ablk;           // 256-wide bf16 tiles: A and B stored tile-contiguous
                           // (256 x 64 blocks, see blk_off in the GEMM source)
+  int32_t nofold;         // 256-wide bf16 tiles: add the input term at the store
+                          // instead of folding it into the accumulators (for
+                          // coefficient ratios that could overflow them)
 };
 
 }  // namespace muon

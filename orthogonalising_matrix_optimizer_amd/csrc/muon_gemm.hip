@@ -653,6 +653,7 @@ struct TileCoef {
   int first;          // first iteration: fold the norm scale s in
   float lr, lrwd;     // FIN: the update's lr and fl(lr * wd)
   int ablk;           // A and B are stored tile-contiguous (256-wide bf16 tiles)
+  int nofold;         // keep the input term out of the accumulators
 };
 
 // One output tile (tP, tQ) of matrix `mat` of group G: K loop and epilogue.
@@ -742,7 +743,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   // 256-wide bf16 tiles fold the input term in during the K loop and store
   // through LDS (APPLY keeps the plain epilogue when beta == 0)
   constexpr bool kStaged = XDT == kBF16 && TS == 256;
-  const bool capt = kStaged && (MODE == POLY || (MODE == APPLY && cf.cbb != 0.f));
+  const bool capt = kStaged && !cf.nofold && (MODE == POLY || (MODE == APPLY && cf.cbb != 0.f));
   const float coef = MODE == POLY ? cf.cb / cf.cc : (capt ? cf.ca / cf.cbb : 0.f);
 
   // the planner pads every dimension to a multiple of 128, so nk is a
@@ -931,6 +932,7 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   cf.eps = args.eps; cf.first = args.first;
   cf.lr = args.lr; cf.lrwd = args.lrwd;
   cf.ablk = args.ablk;
+  cf.nofold = args.nofold;
   gemm_tile<XDT, MODE, TS, WGP, WGQ, FIN>(G, mat, tP, tQ, cf, smem, red);
 }
 

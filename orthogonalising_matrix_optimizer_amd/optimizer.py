@@ -231,14 +231,18 @@ class StepGraph:
     same buffers (parameters, the gradient tensors given at capture, state,
     workspace) with the captured lr, wd, beta, coefficients and weight-average
     flags.  Write new gradients into the captured gradient tensors before a
-    replay.  Host counters advance per replay as for an eager step.  Capture is
+    replay.  Host counters advance per replay as for an eager step (through
+    the library's muon_state_advance).  Eager steps, orthogonalisations and
+    blends on the same optimizer between replays are allowed; capturing
+    another graph on it replaces the table this one replays with.  Capture is
     refused for a step whose weight-average flags would not repeat (the average
     not yet started, or starting at this step): take eager steps first.
     """
 
     def __init__(self, opt: Muon, grads: List[torch.Tensor], lr: Optional[float] = None,
                  wd: Optional[float] = None):
-        st, o = opt.state, opt.opt
+        o = opt.opt
+        st = opt.state
         if o.beta_ema >= 0.0 and o.avg_mode == _lib.MUON_AVG_WEIGHTED:
             raise ValueError("the weighted average changes its coefficients every step; "
                              "a replay would repeat the captured ones")
@@ -248,7 +252,6 @@ class StepGraph:
                                  "(its first step re-initialises it)")
         self.opt = opt
         self.grads = list(grads)
-        self.ema_on = o.beta_ema >= 0.0
         opt.step_prepare(self.grads)
         torch.cuda.synchronize()
         self.g = torch.cuda.CUDAGraph()
@@ -263,9 +266,7 @@ class StepGraph:
         if self._pending:
             self._pending = False
             return
-        self.opt.state.step += 1
-        if self.ema_on:
-            self.opt.state.ema_count += 1
+        _lib.check(self.opt.lib.muon_state_advance(self.opt.state, 1), "muon_state_advance")
 
 
 def _vec(t: torch.Tensor):

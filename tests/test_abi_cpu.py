@@ -427,3 +427,66 @@ def test_rejects_matrices_beyond_32_bit_offsets(lib):
     assert lib.muon_workspace_bytes(ok, 1, opt, 5) > 3 * 2 ** 30
     opt.ns_dtype = _lib.MUON_F32
     assert lib.muon_workspace_bytes(ok, 1, opt, 5) == 0
+
+
+def _layout(lib, shapes, ns=_lib.MUON_BF16):
+    mats = _lib.mat_array((0, r, c, c, _lib.MUON_BF16) for r, c in shapes)
+    opt = _lib.default_options()
+    opt.ns_dtype = ns
+    vals = [ctypes.c_size_t() for _ in range(4)]
+    assert lib.muon_workspace_layout(mats, len(shapes), opt, *[ctypes.byref(v) for v in vals]) == 0
+    return [v.value for v in vals] + [lib.muon_workspace_bytes(mats, len(shapes), opt, 5)]
+
+
+@pytest.mark.parametrize("shapes", [gen.gpt124m_shapes(), [(256, 512)], [(5, 3), (3, 5), (7, 7)],
+                                    gen.moe_share_shapes()])
+def test_table_regions_are_disjoint(lib, shapes):
+    """Uncaptured calls (step, orthogonalise, blend) write the eager table
+    region; captured steps read the capture region, which only
+    muon_step_prepare writes: the two must not overlap each other or the
+    iterate buffers."""
+    eager, capture, tab, buffers, total = _layout(lib, shapes)
+    n = len(shapes)
+    assert tab >= n * 120                         # descriptors of every matrix fit
+    lo, hi = sorted([eager, capture])
+    assert lo + tab <= hi and hi + tab <= buffers <= total
+    assert eager % 256 == 0 and capture % 256 == 0 and buffers % 256 == 0
+
+
+def test_layout_rejects_bad_arguments(lib):
+    v = [ctypes.c_size_t() for _ in range(4)]
+    r = [ctypes.byref(x) for x in v]
+    mats = _lib.mat_array([(0, 0, 4, 4, _lib.MUON_BF16)])
+    assert lib.muon_workspace_layout(mats, 1, None, *r) == E["MUON_E_SHAPE"]
+    assert lib.muon_workspace_layout(None, 1, None, *r) == E["MUON_E_NULL"]
+    mats = _lib.mat_array([(0, 4, 4, 4, _lib.MUON_BF16)])
+    assert lib.muon_workspace_layout(mats, 1, None, None, *r[1:]) == E["MUON_E_NULL"]
+
+
+def test_state_advance_follows_the_step_rules(lib):
+    st = _lib.MuonState()
+    st.opt = _lib.default_options()
+    st.step = 7
+    assert lib.muon_state_advance(ctypes.byref(st), 3) == 0
+    assert st.step == 10 and st.ema_count == 0
+    assert lib.muon_state_advance(ctypes.byref(st), -1) == E["MUON_E_HPARAM"]
+    assert lib.muon_state_advance(None, 1) == E["MUON_E_NULL"]
+    # exponential average started at step 5: each replay folds into it
+    st.opt.beta_ema = 0.99
+    st.opt.ema_start = 5
+    st.ema_count = 6
+    assert lib.muon_state_advance(ctypes.byref(st), 2) == 0
+    assert st.step == 12 and st.ema_count == 8
+    # an average that has not started could not have been captured
+    st.ema_count = 0
+    st.step = 1
+    assert lib.muon_state_advance(ctypes.byref(st), 1) == E["MUON_E_CAPTURE"]
+    assert st.step == 1 and st.ema_count == 0
+    # neither could a weighted running mean
+    st.ema_count = 3
+    st.step = 9
+    st.opt.avg_mode = _lib.MUON_AVG_WEIGHTED
+    assert lib.muon_state_advance(ctypes.byref(st), 1) == E["MUON_E_CAPTURE"]
+    assert st.step == 9 and st.ema_count == 3
+    st.opt.avg_mode = 7
+    assert lib.muon_state_advance(ctypes.byref(st), 1) == E["MUON_E_HPARAM"]

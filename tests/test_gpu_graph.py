@@ -120,3 +120,51 @@ def test_c_abi_refuses_capture_of_weighted_average_steps():
     torch.cuda.synchronize()
     assert opt.step_count == 1 and opt.ema_count == 1
     assert all(torch.equal(a, b) for a, b in zip(before, p))
+
+
+def test_graph_replays_survive_blends_and_eager_calls_on_the_workspace():
+    """Between replays: a readout blend, an eager step on other gradient
+    buffers and an orthogonalisation through the same workspace.  Those calls
+    send their own descriptor tables; the replayed step must still read the
+    one muon_step_prepare sent (a separate region of the workspace) and stay
+    bit for bit equal to an eager twin that makes the same calls."""
+    announce("graph: replays with blends and eager calls in between")
+    kw = dict(lr=0.02, wd=0.1, beta=0.9, steps=5, beta_ema=0.99, ema_start=1)
+    pa = _params(12)
+    pb = [p.clone() for p in pa]
+    A = mo.Muon(pa, **kw)
+    B = mo.Muon(pb, **kw)
+    static = [torch.empty_like(g) for g in _grads(12, 0)]
+    g = _grads(12, 0)
+    A.step(g)
+    B.step(g)
+    graph = B.graph(static)
+    for t in range(1, 5):
+        g = _grads(12, t)
+        for dst, src in zip(static, g):
+            dst.copy_(src)
+        A.step(g)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert _same(pa, pb), t
+        assert _same(A.mom, B.mom) and _same(A.ema, B.ema), t
+        assert (A.step_count, A.ema_count) == (B.step_count, B.ema_count), t
+        # calls that send other tables into the same workspaces
+        oa = [torch.empty(p.shape, dtype=torch.float32, device="cuda") for p in pa]
+        ob = [torch.empty_like(x) for x in oa]
+        A.blend(oa, 0.35)
+        B.blend(ob, 0.35)
+        torch.cuda.synchronize()
+        assert _same(oa, ob), t
+        if t % 2:
+            other = _grads(13, t)
+            A.step(other)
+            B.step(other)
+        ins = _grads(14, t)
+        ua = [torch.empty(p.shape, dtype=torch.float32, device="cuda") for p in pa]
+        ub = [torch.empty_like(x) for x in ua]
+        mo.orthogonalize(ins, ua, steps=5, workspace=A.workspace)
+        mo.orthogonalize(ins, ub, steps=5, workspace=B.workspace)
+        torch.cuda.synchronize()
+        assert _same(ua, ub), t
+        assert _same(pa, pb), t
