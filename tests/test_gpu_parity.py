@@ -97,6 +97,58 @@ def test_mixed_coefficient_table(tile, ns, tol):
     for u, o in zip(us, outs):
         ref = orc.orthogonalize(u.astype(np.float64), table)
         assert orc.rel_fro(host(o), ref) <= tol, u.shape
+        assert sigma_dev(host(o), ref) <= TOL_SIGMA, u.shape
+
+
+@pytest.mark.parametrize("tile", [256], indirect=True)
+def test_tiny_coefficient_ratios_run_unfolded(tile):
+    """The 256-wide bf16 products fold the term bA (or aX) into their
+    accumulators as (b/c)A (or (a/b)X).  Rows where that ratio would overflow
+    fp32 -- c tiny or subnormal, a cubic row with tiny b -- must give the
+    oracle's result (the library then adds the term at the store), and the
+    step keeps its separate finish kernel."""
+    announce(f"orthogonalize tiny coefficient ratios tile={tile}")
+    rows = [gen.QUINTIC, (1.875, -1.25, 1e-30), (1.5, 1e-38, 0.0), gen.QUINTIC,
+            (1.5, -0.5, 1e-40)]
+    # the library takes fp32 coefficients: the oracle gets the same values
+    table = np.array(rows, dtype=np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        assert np.float32(1e-40) != 0 and np.isinf(np.float32(-1.25) / np.float32(1e-40))
+    shapes = [(768, 3072), (3072, 768), (300, 520), (256, 256)]
+    us = [gen.grad_matrix(r, c, 6, 0, i).astype(np.float32) for i, (r, c) in enumerate(shapes)]
+    ins = [dev_f32(u) for u in us]
+    outs = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in ins]
+    mo.orthogonalize(ins, outs, coeffs=table, steps=len(table), ns_dtype="bf16")
+    torch.cuda.synchronize()
+    for u, o in zip(us, outs):
+        O = host(o)
+        assert np.all(np.isfinite(O)), u.shape
+        ref = orc.orthogonalize(u.astype(np.float64), table)
+        assert orc.rel_fro(O, ref) <= TOL_BF16, u.shape
+        assert sigma_dev(O, ref) <= TOL_SIGMA, u.shape
+    info = mo.plan_info(shapes, len(table), table)
+    assert info["tile"] == 256
+    # prepare, four rows with a polynomial launch, one without, and a separate
+    # finish launch (the update cannot run in the last product's epilogue)
+    assert info["launches_per_step"] == 2 + 4 * 3 + 2
+    # a full step with this table against the oracle's fp32 update of the same O
+    gs, ws = _make([(768, 3072), (512, 256)], "bf16")
+    params = [_dev(w) for w in ws]
+    opt = mo.Muon(params, lr=0.02, wd=0.1, beta=0.95, steps=len(table), coeffs=table,
+                  diagnostics=False)
+    twin = [p.clone() for p in params]
+    opt_t = mo.Muon(twin, lr=0.02, wd=0.1, beta=0.95, steps=len(table), coeffs=table,
+                    diagnostics=True)
+    grads = [_dev(g) for g in gs]
+    opt.step(grads)
+    opt_t.step(grads)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        O = host(opt_t.update[i])
+        assert np.all(np.isfinite(O))
+        want = orc.store(orc.update_f32(_val(w), O, 0.02, 0.1), "bf16").astype(np.float32)
+        np.testing.assert_array_equal(host(opt_t.params[i]), want)
+        assert torch.equal(params[i], twin[i])
 
 
 def test_bf16_inputs_and_outputs():
@@ -108,6 +160,7 @@ def test_bf16_inputs_and_outputs():
     for u, o in zip(us, outs):
         ref = orc.orthogonalize(gen.f32_from_bf16_bits(u).astype(np.float64), _table("quintic", 6))
         assert orc.rel_fro(o, ref) <= TOL_BF16
+        assert sigma_dev(o, ref) <= TOL_SIGMA
 
 
 @pytest.mark.parametrize("ns,tol", [("f32", 1e-6), ("bf16", 5e-3)])
@@ -119,6 +172,7 @@ def test_zero_steps_is_normalisation(ns, tol):
     for u, o in zip(us, outs):
         ref = u.astype(np.float64) / (np.linalg.norm(u.astype(np.float64)) + 1e-7)
         assert orc.rel_fro(o, ref) <= tol
+        assert sigma_dev(o, ref) <= TOL_SIGMA
 
 
 def test_cubic_converges_to_polar_factor():
@@ -237,6 +291,7 @@ def test_anvil_ten_steps_state_forced():
             O = host(opt.update[i])
             ref = orc.orthogonalize(M[i].astype(np.float64), coeffs)
             assert orc.rel_fro(O, ref) <= TOL_BF16
+            assert sigma_dev(O, ref) <= TOL_SIGMA
             Wn = orc.store(orc.update_f32(W[i], O, lr, wd, mask), "bf16").astype(np.float32)
             np.testing.assert_array_equal(host(params[i]), Wn)
             E[i] = Wn.copy() if t == 1 else orc.ema_f32(E[i], Wn, be)
@@ -313,6 +368,7 @@ def test_nesterov():
     ref = orc.orthogonalize(U.astype(np.float64), _table("quintic", 5))
     np.testing.assert_array_equal(host(opt.mom[0]), M)
     assert orc.rel_fro(host(opt.update[0]), ref) <= TOL_BF16
+    assert sigma_dev(host(opt.update[0]), ref) <= TOL_SIGMA
 
 
 def test_zero_gradient_pure_decay():
@@ -475,6 +531,7 @@ def test_strided_views_match_oracle(dtype):
         np.testing.assert_array_equal(host(opt.mom[i]), st.mom[i])
         O = host(opt.update[i])
         assert orc.rel_fro(O, ref["O"][i]) <= TOL_BF16, shapes[i]
+        assert sigma_dev(O, ref["O"][i]) <= TOL_SIGMA, shapes[i]
         want = orc.store(orc.update_f32(w0[i], O, lr, wd), dtype)
         np.testing.assert_array_equal(host(params[i]).astype(np.float64), want)
         pb, gb, po, go = bufs[i]
