@@ -14,10 +14,15 @@ gpt2p7b (32 layers x {4x 2560^2, 2560x10240, 10240x2560}, wd 1.6) and
 moe_share (64 experts x {2048x1408, 1408x2048} + 24 x 4 x 2048^2).
 
 Prints one JSON line.  Extra fields: NS TFLOP/s (symmetric flop count),
-per-kernel times, the roofline of the dominant kernel (the APPLY GEMM,
-timed live with HIP events around its launches in the timed region), the
-step replayed from one captured device graph, a single 256x512 matrix eager
-and replayed, and the CPU oracle timed on the host on the same workload.
+per-kernel times, elementwise GB/s, the roofline of the dominant kernel (the
+APPLY GEMM, timed live with HIP events around its launches in the timed
+region), the step replayed from one captured device graph, `configs` (the
+same record for the other matrix sets: the ANVIL option set, the 2.7B set
+and the MoE share, each timed the same way after the main line), a single
+256x512 matrix eager and replayed, AdamW over the 124M model's other
+parameters, and the CPU oracle timed on the host: one whole step for the
+124M sets, one matrix per distinct shape (labelled as an estimate for the
+whole step) for the 2.7B and MoE sets.
 """
 from __future__ import annotations
 
@@ -93,11 +98,12 @@ def elementwise_bytes(shapes, ms):
     return prep * n, fin * n
 
 
-def cpu_baseline(ms, coeffs, budget_s: float = 20.0):
-    """The CPU oracle (fp64 numpy) on the same step.  The 124M set runs one
-    whole step; for larger sets the oracle steps through the matrices in
-    order until `budget_s` seconds have passed and the rate is scaled by the
-    Newton-Schulz flop count of the whole set (stated in `sample`)."""
+def cpu_baseline(ms, coeffs, whole_step: bool):
+    """The CPU oracle (fp64 numpy, the float32 state recurrences) on the same
+    step.  whole_step: one whole step of the set, measured.  Otherwise (sets
+    whose oracle step takes minutes) one matrix of each distinct shape is
+    measured and the step's time is estimated as the sum over shapes of the
+    measured time times the shape's matrix count; the record says so."""
     import threadpoolctl
     from oracle import muon_oracle as orc
     from workloads import gen
@@ -106,9 +112,15 @@ def cpu_baseline(ms, coeffs, budget_s: float = 20.0):
     vendor = ",".join(sorted({str(i.get("internal_api")) for i in info
                               if i.get("user_api") == "blas"})) or "unknown"
     shapes = list(ms.shapes)
-    total_fl = sum(orc.ns_flops_dense(r, c, ms.steps) for r, c in shapes)
-    done_fl, done, dt = 0.0, 0, 0.0
-    for i in range(len(shapes)):
+    if whole_step:
+        idx = list(range(len(shapes)))
+    else:
+        first = {}
+        for i, s in enumerate(shapes):
+            first.setdefault(s, i)
+        idx = list(first.values())
+    times = {}
+    for i in idx:
         (g, w), = gen.make_inputs(ms, seed=0, indices=[i])
         st = orc.OracleState([shapes[i]], beta_slow=ms.beta_slow, beta_ema=ms.beta_ema,
                              ema_start=ms.ema_start)
@@ -116,18 +128,24 @@ def cpu_baseline(ms, coeffs, budget_s: float = 20.0):
         orc.muon_step([gen.f32_from_bf16_bits(w).astype(np.float64)], [gen.f32_from_bf16_bits(g)],
                       st, coeffs, ms.lr, ms.wd, ms.beta, param_dtype="bf16",
                       cautious=ms.cautious, keep=False)
-        dt += time.perf_counter() - t0
-        done_fl += orc.ns_flops_dense(*shapes[i], ms.steps)
-        done += 1
-        if dt > budget_s:
-            break
-    est = dt * total_fl / done_fl
-    sample = (f"one full step of the same {len(shapes)}-matrix set on the host ({dt:.2f} s"
-              if done == len(shapes) else
-              f"{done} of the {len(shapes)} matrices of one step on the host ({dt:.2f} s), "
-              f"scaled to the whole set by Newton-Schulz flops (estimated {est:.1f} s per step")
+        times[i] = time.perf_counter() - t0
+    measured = sum(times.values())
+    if whole_step:
+        est = measured
+        sample = (f"one whole step of the same {len(shapes)}-matrix set on the host, measured "
+                  f"({measured:.2f} s")
+    else:
+        count = {}
+        for s in shapes:
+            count[s] = count.get(s, 0) + 1
+        est = sum(times[i] * count[shapes[i]] for i in idx)
+        sample = (f"{len(idx)} of the {len(shapes)} matrices measured (one per distinct shape: "
+                  + ", ".join(f"{shapes[i][0]}x{shapes[i][1]} {times[i]:.2f} s" for i in idx)
+                  + f"); the whole step is an ESTIMATE, each shape's time times its matrix "
+                    f"count ({est:.1f} s")
     return {"value": round(1.0 / est, 5), "unit": "optimizer steps/s", "cores": int(threads),
-            "kind": "oracle", "sample": sample + f", fp64 numpy, BLAS {vendor})"}
+            "kind": "oracle", "measured_s": round(measured, 3), "estimated": not whole_step,
+            "sample": sample + f", fp64 numpy, BLAS {vendor})"}
 
 
 def _events_ms(fn, reps):
@@ -216,38 +234,12 @@ def adamw_times(gen, mo, dev, reps):
             "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="gpt124m", choices=sorted(WORKLOADS),
-                    help="matrix set and options of the step (default: the 124M set)")
-    ap.add_argument("--copy-calib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("this benchmark runs on one GPU only: the optimizer step is measured on a single "
-              "MI355X (the multi-GPU layout is a design note, not a measured path)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, steps, warmup, mo, gen, dev, with_graph=False):
+    """Time `steps` optimizer steps of matrix set `name` after `warmup` steps
+    (inputs resident in HBM), with HIP events around every APPLY launch of the
+    timed region, then per-phase kernel times from a short extra run."""
     import torch
-    import orthogonalising_matrix_optimizer_amd as mo
-    from workloads import gen
-
-    dev = torch.device("cuda:0")
-    if args.copy_calib:
-        n = args.copy_calib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
-        return
-
-    ms = gen.SETS[args.workload]
+    ms = gen.SETS[name]
     shapes = list(ms.shapes)
     coeffs = gen.coeff_table(ms.coeffs, ms.steps)
     if ms.numel <= 200_000_000:
@@ -272,26 +264,26 @@ def main():
     plan = mo.plan_info(shapes, ms.steps, coeffs)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         opt.step(grads)
     torch.cuda.synchronize()
 
     # timed region; the APPLY launches are bracketed with HIP events on the
     # launch stream (a last APPLY that carries the parameter update is a
     # separate kernel and phase, apply_update)
-    n_apply = args.steps * ms.steps
+    n_apply = steps * ms.steps
     mo.probe_arm("apply", n_apply)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         opt.step(grads)
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
-    per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
+    ms_step = ev[0].elapsed_time(ev[-1]) / steps
+    per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
     apply_ms = mo.probe_read(n_apply)
     mo.probe_disarm()
 
@@ -308,39 +300,27 @@ def main():
         phase_ms[ph] = round(float(np.mean(t)), 4) if t else None
     phase_ms["apply"] = round(float(np.mean(apply_ms)), 4) if apply_ms else None
 
-    # the same step captured once as a device graph and replayed (not part of
-    # `value`); and the single 256x512 fp32 matrix, eager and replayed, where
-    # launch latency dominates
-    graph_ms = time_graph(opt, grads, args.steps) if ms.beta_ema < 0 or opt.ema_count > 0 else None
-    c1 = single_matrix_times(gen, mo, dev, args.steps, with_oracle=not args.no_cpu_baseline)
-    adamw = adamw_times(gen, mo, dev, max(args.steps, 20))
+    graph_ms = None
+    if with_graph and (ms.beta_ema < 0 or opt.ema_count > 0):
+        graph_ms = time_graph(opt, grads, steps)
 
     sym, dense = gen.ns_flops(shapes, ms.steps)
     a_flops = apply_flops(shapes)
     a_tf = a_flops / (phase_ms["apply"] * 1e-3) / 1e12
-    key = f"{args.workload}:{ms.steps}:{ms.coeffs}"
-    traffic = _traffic(args.workload, key)
+    traffic = _traffic(name, f"{name}:{ms.steps}:{ms.coeffs}")
     prep_b, fin_b = elementwise_bytes(shapes, ms)
-    steps_per_s = 1000.0 / ms_step
-    out = {
-        "metric": "optimizer steps/sec + NS TFLOP/s (% MFMA peak), 124M-GPT matrix set, 1 GPU"
-                  if args.workload == "gpt124m" else
-                  f"optimizer steps/sec + NS TFLOP/s (% MFMA peak), {args.workload} matrix set, 1 GPU",
-        "value": round(steps_per_s, 3),
+    prep_gbs = prep_b / (phase_ms["prepare"] * 1e-3) / 1e9
+    fin_gbs = fin_b / (phase_ms["finish"] * 1e-3) / 1e9 if phase_ms["finish"] else None
+    rec = {
+        "workload": WORKLOADS[name],
+        "value": round(1000.0 / ms_step, 3),
         "unit": "optimizer steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_p10_median_p90": [round(float(np.percentile(per_step, q)), 4)
                                        for q in (10, 50, 90)],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded low-rank+noise gradients, random-init bf16 parameters)",
-        "config": {"workload": WORKLOADS[args.workload],
-                   "matrices": len(shapes), "elements": int(sum(r * c for r, c in shapes)),
+        "config": {"matrices": len(shapes), "elements": int(sum(r * c for r, c in shapes)),
                    "ns_steps": ms.steps, "coeffs": "quintic (15/8, -10/8, 3/8)",
                    "groups": plan["groups"], "tile": plan["tile"],
                    "launches_per_step": plan["launches_per_step"]},
@@ -348,10 +328,11 @@ def main():
         "ns_frac_mfma_peak": round(sym / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ns_flops_per_step": {"symmetric": sym, "dense_equivalent": dense},
         "kernel_ms": phase_ms,
-        "elementwise_gbs": {
-            "prepare": round(prep_b / (phase_ms["prepare"] * 1e-3) / 1e9, 1),
-            "finish": (round(fin_b / (phase_ms["finish"] * 1e-3) / 1e9, 1)
-                       if phase_ms["finish"] else None)},
+        "elementwise_gbs": {"prepare": round(prep_gbs, 1),
+                            "finish": round(fin_gbs, 1) if fin_gbs else None},
+        "elementwise_frac_hbm_peak": {"prepare": round(prep_gbs / PEAK_HBM_GBS, 4),
+                                      "finish": round(fin_gbs / PEAK_HBM_GBS, 4) if fin_gbs
+                                      else None},
         # the plain update runs in the last APPLY launch's epilogue (no finish
         # launch); that launch is timed as apply_update, not in apply/roofline
         "update_in_last_apply": phase_ms["apply_update"] is not None,
@@ -361,11 +342,99 @@ def main():
                      "flops_per_launch": a_flops, "launches_timed": len(apply_ms)},
         "wall_s_timed": round(wall, 4),
         "graph_ms_per_step": graph_ms,
-        "single_matrix": c1,
-        "adamw": adamw,
     }
+    del opt, params, grads
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="gpt124m", choices=sorted(WORKLOADS),
+                    help="matrix set and options of the step (default: the 124M set)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="leave out the records of the other matrix sets and the extras "
+                         "(single matrix, AdamW, graph replay)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("this benchmark runs on one GPU only: the optimizer step is measured on a single "
+              "MI355X (the multi-GPU layout is a design note, not a measured path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import orthogonalising_matrix_optimizer_amd as mo
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
+        return
+
+    name = args.workload
+    main_rec = measure(name, args.steps, args.warmup, mo, gen, dev,
+                       with_graph=not args.no_configs)
+    out = {
+        "metric": "optimizer steps/sec + NS TFLOP/s (% MFMA peak), 124M-GPT matrix set, 1 GPU"
+                  if name == "gpt124m" else
+                  f"optimizer steps/sec + NS TFLOP/s (% MFMA peak), {name} matrix set, 1 GPU",
+        "value": main_rec["value"],
+        "unit": "optimizer steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_rec["ms_per_step"],
+        "ms_per_step_p10_median_p90": main_rec["ms_per_step_p10_median_p90"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded low-rank+noise gradients, random-init bf16 parameters)",
+        "config": dict({"workload": main_rec["workload"]}, **main_rec["config"]),
+    }
+    for k in ("ns_tflops", "ns_frac_mfma_peak", "ns_flops_per_step", "kernel_ms",
+              "elementwise_gbs", "elementwise_frac_hbm_peak", "update_in_last_apply",
+              "roofline", "wall_s_timed", "graph_ms_per_step"):
+        out[k] = main_rec[k]
+    if not args.no_configs:
+        # the other matrix sets of the same step, each timed the same way
+        # (fewer steps for the 2.7B set, whose step takes ~0.1 s)
+        others = {}
+        for other in ("gpt124m_anvil", "gpt2p7b", "moe_share"):
+            if other == name:
+                continue
+            st = min(args.steps, 10) if other == "gpt2p7b" else args.steps
+            wu = min(args.warmup, 3) if other == "gpt2p7b" else args.warmup
+            others[other] = measure(other, st, wu, mo, gen, dev)
+            print(f"measured {other}: {others[other]['ms_per_step']} ms per step",
+                  file=sys.stderr, flush=True)
+        out["configs"] = others
+        out["single_matrix"] = single_matrix_times(gen, mo, dev, args.steps,
+                                                   with_oracle=not args.no_cpu_baseline)
+        out["adamw"] = adamw_times(gen, mo, dev, max(args.steps, 20))
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(ms, coeffs)
+        coeffs = gen.coeff_table(gen.SETS[name].coeffs, gen.SETS[name].steps)
+        out["cpu_baseline"] = cpu_baseline(gen.SETS[name], coeffs,
+                                           whole_step=gen.SETS[name].numel <= 200_000_000)
+        if not args.no_configs:
+            for other, rec in out["configs"].items():
+                ms = gen.SETS[other]
+                rec["cpu_baseline"] = cpu_baseline(ms, gen.coeff_table(ms.coeffs, ms.steps),
+                                                   whole_step=ms.numel <= 200_000_000)
+                print(f"oracle {other}: {rec['cpu_baseline']['measured_s']} s measured",
+                      file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
