@@ -176,6 +176,25 @@ int muon_step(const muon_mat* params, const muon_mat* grads, muon_state* st,
               const float* coeffs, int32_t steps, float lr, float wd,
               float beta, void* stream);
 
+/* Allocation-free step, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it).  Same
+ * arguments, validation, arithmetic and results as muon_step, but
+ * st->workspace and st->workspace_bytes are ignored: the workspace is a
+ * static device array of the library of MUON_NOALLOC_SCRATCH_BYTES (64 MiB),
+ * one per GPU, held from the first call on that GPU until the process ends
+ * (the current device when the call is made).  The descriptor table is
+ * written into it by kernels on `stream`, so the call uses no pinned staging
+ * memory, calls no allocation routine and may run under stream capture.  A
+ * step whose muon_workspace_bytes exceeds MUON_NOALLOC_SCRATCH_BYTES returns
+ * MUON_E_WORKSPACE and enqueues nothing.  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (each call rewrites every
+ * byte it reads): calls that may overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller. */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+int muon_step_noalloc(const muon_mat* params, const muon_mat* grads, muon_state* st,
+                      const float* coeffs, int32_t steps, float lr, float wd, float beta,
+                      void* stream);
+
 /* Graph capture of a step (page "Training NanoGPT in 39.9 Seconds", Table A,
  * credits capturing the training step as a device graph with part of the
  * end-to-end gain).  Besides its kernel launches, muon_step enqueues one

@@ -22,6 +22,7 @@ CODES = {v: k for k, v in STATUS.items()}
 PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4, "adamw": 5,
           "apply_update": 6}
 MAX_STEPS = 16
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MuonMat(ctypes.Structure):
@@ -105,6 +106,9 @@ def load() -> ctypes.CDLL:
     lib.muon_plan_info.argtypes = [P(MuonMat), c_int32, P(MuonOptions), c_int32, P(c_float),
                                    P(c_int32), P(c_int32), c_int32, P(c_int32)]
     lib.muon_plan_info.restype = c_int32
+    lib.muon_step_noalloc.argtypes = [P(MuonMat), P(MuonMat), P(MuonState), P(c_float), c_int32,
+                                      c_float, c_float, c_float, c_void_p]
+    lib.muon_step_noalloc.restype = c_int32
     lib.muon_state_advance.argtypes = [P(MuonState), c_int32]
     lib.muon_state_advance.restype = c_int32
     lib.muon_workspace_layout.argtypes = [P(MuonMat), c_int32, P(MuonOptions), P(c_size_t),

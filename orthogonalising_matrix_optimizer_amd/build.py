@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuon_mi355x.so")
-SOURCES = ["muon_elem.hip", "muon_gemm.hip", "muon_api.cpp"]
+SOURCES = ["muon_elem.hip", "muon_gemm.hip", "muon_noalloc.hip", "muon_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

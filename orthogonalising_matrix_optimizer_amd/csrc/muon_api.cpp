@@ -599,10 +599,20 @@ size_t muon_workspace_bytes(const muon_mat* params, int32_t n, const muon_option
 }
 
 namespace {
+// A workspace that is not the state's: the library's static scratch of the
+// allocation-free entry point.  Its descriptor table is written by kernels
+// (launch_put_table) instead of a copy from pinned staging memory.
+struct FixedWorkspace {
+  void* ptr;
+  size_t bytes;
+};
+
 // muon_step, or with prepare_only its validation and descriptor-table upload
-// alone (no launch, counters unchanged).
+// alone (no launch, counters unchanged).  fixed: use that workspace instead
+// of st->workspace (never with prepare_only).
 int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, const float* coeffs,
-              int32_t steps, float lr, float wd, float beta, void* stream, bool prepare_only) {
+              int32_t steps, float lr, float wd, float beta, void* stream, bool prepare_only,
+              const FixedWorkspace* fixed = nullptr) {
   if (!st) return MUON_E_NULL;
   const int n = st->n;
   if (n < 0) return MUON_E_SHAPE;
@@ -659,8 +669,8 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
     rows[i] = params[i].rows;
     cols[i] = params[i].cols;
   }
-  void* const wsp = st->workspace;
-  const size_t ws_bytes = st->workspace_bytes;
+  void* const wsp = fixed ? fixed->ptr : st->workspace;
+  const size_t ws_bytes = fixed ? fixed->bytes : st->workspace_bytes;
   if (!wsp) return MUON_E_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_mu);
   const Plan& p = get_plan(rows.data(), cols.data(), n, o.ns_dtype);
@@ -701,11 +711,20 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
   // the weighted average's coefficients change with every step: a replayed
   // capture would repeat stale ones
   if (weighted && capturing && !prepare_only) return MUON_E_CAPTURE;
-  // muon_step_prepare fills the capture region, which captured steps read;
-  // uncaptured steps send and read the eager region
-  const char* tab = ws + p.off_tab[(prepare_only || capturing) ? kTabCapture : kTabEager];
-  if ((rc = upload_table(const_cast<char*>(tab), bytes, s)) != MUON_OK) return rc;
-  if (prepare_only) return MUON_OK;
+  const char* tab;
+  if (fixed) {
+    // the static scratch: the table is written by kernels on the stream (part
+    // of a capture when the stream is capturing)
+    tab = ws + p.off_tab[kTabEager];
+    if (launch_put_table(const_cast<char*>(tab), bytes.data(), bytes.size(), s) != hipSuccess)
+      return MUON_E_HIP;
+  } else {
+    // muon_step_prepare fills the capture region, which captured steps read;
+    // uncaptured steps send and read the eager region
+    tab = ws + p.off_tab[(prepare_only || capturing) ? kTabCapture : kTabEager];
+    if ((rc = upload_table(const_cast<char*>(tab), bytes, s)) != MUON_OK) return rc;
+    if (prepare_only) return MUON_OK;
+  }
 
   ElemArgs ea;
   std::memset(&ea, 0, sizeof(ea));
@@ -772,6 +791,18 @@ int muon_step_prepare(const muon_mat* params, const muon_mat* grads, muon_state*
   return step_impl(params, grads, st, nullptr, 0, 0.f, 0.f, 0.f, stream, true);
 }
 
+}  // extern "C"
+
+namespace muon {
+int step_fixed_workspace(const muon_mat* params, const muon_mat* grads, muon_state* st,
+                         const float* coeffs, int32_t steps, float lr, float wd, float beta,
+                         void* stream, void* ws, size_t ws_bytes) {
+  const FixedWorkspace f{ws, ws_bytes};
+  return step_impl(params, grads, st, coeffs, steps, lr, wd, beta, stream, false, &f);
+}
+}  // namespace muon
+
+extern "C" {
 
 int muon_state_advance(muon_state* st, int32_t replays) {
   if (!st) return MUON_E_NULL;

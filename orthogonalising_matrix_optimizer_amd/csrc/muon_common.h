@@ -151,6 +151,10 @@ hipError_t launch_prepare(const ElemArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_finish(const ElemArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,
                         hipStream_t s);
+// Write `n` bytes (a multiple of 4) of a host table to device memory at `dst`
+// (4-byte aligned) with kernels that carry the bytes as arguments: no host
+// staging memory, ordered on the stream like the launches that read it.
+hipError_t launch_put_table(void* dst, const uint8_t* bytes, size_t n, hipStream_t s);
 // phase: 0 GRAM, 1 POLY, 2 APPLY; ts: tile edge (64, 128; 256 for bf16 only);
 // waves: 8 for 256-wide tiles, else 4.
 hipError_t launch_gemm(int phase, int xdt, int ts, int waves, const GemmArgs& a,
