@@ -500,6 +500,10 @@ hipError_t run_ns(const Plan& p, char* ws, const char* tab, const float* coeffs,
           char* xin = ws + (cur ? g.off_x1 : g.off_x0);
           char* xout = ws + (cur ? g.off_x0 : g.off_x1);
           d.count = int(g.mats.size());
+          // K loops stop at the real contraction length (rounded to the
+          // two-stage pipeline's 128): a 1408-row group padded to 1536 for
+          // 256-wide tiles runs 22 stages of 64, not 24
+          d.kdim = int(round_up(phase == 0 ? g.n : g.m, 128));
           d.mp = g.mp; d.np = g.np;
           d.partials = reinterpret_cast<const float*>(ws + g.off_part);
           d.p_stride = g.npart;

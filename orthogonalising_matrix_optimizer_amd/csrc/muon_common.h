@@ -94,6 +94,10 @@ struct GemmGroup {
   int32_t tiles;          // tiles per matrix
   int32_t block_base;     // first block of this group in the launch
   int32_t npartials;
+  int32_t kdim;           // contraction length run by the K loop: the unpadded
+                          // contraction dimension rounded up to 128 (n for GRAM,
+                          // m for POLY and APPLY); the zero padding beyond it
+                          // contributes nothing
   const FinDesc* fin;     // fused update: one entry per matrix of the group
 };
 

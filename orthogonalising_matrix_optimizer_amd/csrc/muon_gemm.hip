@@ -700,7 +700,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
   int K;
   if (MODE == GRAM || MODE == POLY) {
     const int ld = MODE == GRAM ? G.np : G.mp;
-    K = ld;
+    K = G.kdim;
     const uint32_t bytes = static_cast<uint32_t>(G.mp) * ld * ES;
     la.rs = make_desc(xin, bytes);
     lb.rs = la.rs;
@@ -716,7 +716,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& G, int mat, int tP, i
     plan_kc<CPR>(la, lane, wave);
     plan_kc<CPR>(lb, lane, wave);
   } else {
-    K = G.mp;
+    K = G.kdim;
     la.rs = make_desc(xin, static_cast<uint32_t>(G.mp) * G.np * ES);
     la.ld_bytes = static_cast<uint32_t>(G.np) * ES;
     la.origin = static_cast<uint32_t>(tP) * TS * ES;
