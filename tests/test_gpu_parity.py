@@ -242,17 +242,17 @@ def test_step_matches_oracle(dtype, ns):
         want = orc.store(orc.update_f32(w0[i], O, lr, wd), dtype)
         np.testing.assert_array_equal(host(params[i]).astype(np.float64), want)
         assert np.all(host(opt.mask[i]) == 1)
-        # free-running: both sides round once to the storage type (at most one
-        # unit in the last place of the larger of the two values; fp32 storage
-        # also carries the fp32 operation rounding, a few units) on top of
-        # lr times the deviation of O
+        # free-running: on top of lr times the deviation of O, the device's
+        # three fp32 operations round at the scale of their operands (W_{t-1}
+        # and lr*O, which matters where they nearly cancel) and both sides
+        # round once to the storage type (half a unit each, so one unit of the
+        # larger result between them)
         w = host(params[i]).astype(np.float64)
         wr = ref["params"][i]
-        # fp32 intermediates round at the scale of the largest operand, which
-        # matters where W_{t-1} and lr*O nearly cancel
-        big = np.maximum.reduce([np.abs(w), np.abs(wr), np.abs(w0[i]),
-                                 np.abs(lr32 * O)]).astype(np.float32)
-        ulp = np.spacing(big).astype(np.float64) * (2 ** 16 if dtype == "bf16" else 4)
+        res = np.maximum(np.abs(w), np.abs(wr)).astype(np.float32)
+        ops = np.maximum(np.abs(w0[i]), np.abs(lr32 * O)).astype(np.float32)
+        unit = np.spacing(res).astype(np.float64) * (2 ** 16 if dtype == "bf16" else 1)
+        ulp = unit + 4 * np.spacing(ops).astype(np.float64)
         dev = np.abs(O - ref["O"][i])
         excess = np.abs(w - wr) - (ulp + lr32 * dev)
         assert np.all(excess <= 1e-12), (shapes[i], float(excess.max()))
