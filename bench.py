@@ -360,6 +360,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="leave out the records of the other matrix sets and the extras "
                          "(single matrix, AdamW, graph replay)")
+    ap.add_argument("--single-only", action="store_true",
+                    help="only time the single 256x512 matrix step (eager and replayed)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -381,6 +383,11 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
+        return
+
+    if args.single_only:
+        print(json.dumps(single_matrix_times(gen, mo, dev, args.steps,
+                                             with_oracle=not args.no_cpu_baseline)), flush=True)
         return
 
     name = args.workload
