@@ -265,8 +265,10 @@ enum {
   MUON_PHASE_APPLY = 3,    /* X <- a X + B X                          */
   MUON_PHASE_FINISH = 4,   /* update, mask, EMA (or write O)          */
   MUON_PHASE_ADAMW = 5,    /* the AdamW kernel of muon_adamw_step     */
-  MUON_PHASE_APPLY_UPDATE = 6  /* last APPLY with the plain update of W
+  MUON_PHASE_APPLY_UPDATE = 6, /* last APPLY with the plain update of W
                                   (see muon_step); not in MUON_PHASE_APPLY */
+  MUON_PHASE_NS_SINGLE = 7     /* all iterations of a small problem in one
+                                  launch (see muon_plan_info)            */
 };
 
 /* Record events around each of the next `capacity` launches of `phase`
@@ -302,7 +304,18 @@ int muon_workspace_layout(const muon_mat* params, int32_t n, const muon_options*
  * block-order bits of the GRAM, POLY and APPLY launches (1 plain, 2 row-major
  * APPLY tiles, 4 whole matrices dealt to XCDs, 8 APPLY by column panel).
  * Results do not depend on MUON_GEMM_ORDER; MUON_TILE changes the rounding of
- * the bf16 path within its tolerance. */
+ * the bf16 path within its tolerance.
+ * With MUON_NS_SINGLE_LAUNCH=1 (read at every call), small problems (64-wide
+ * tiles with bf16 operands, at most 1024 tiles per product, at most 16
+ * iterations) run all Newton-Schulz iterations in one launch whose blocks
+ * meet at a grid-wide barrier between products; it computes every tile as the
+ * separate launches do, so results are the same bit for bit, and counts as
+ * one launch here.  It is not the default: on MI355X the barriers (device-
+ * scope release and acquire across the XCDs' caches) cost more than the
+ * kernel boundaries they replace.  The barrier's wait is bounded
+ * (MUON_NS_SPIN_LIMIT polls, read at every call; 0 gives up at once): a block
+ * that gives up marks the step failed and the finish kernel then writes NaN
+ * for every O, so such a failure is never silent. */
 int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt,
                    int32_t steps, const float* coeffs, int32_t* n_groups,
                    int32_t* tiles, int32_t cap, int32_t* launches_per_step);

@@ -20,7 +20,7 @@ STATUS = {
 }
 CODES = {v: k for k, v in STATUS.items()}
 PHASES = {"prepare": 0, "gram": 1, "poly": 2, "apply": 3, "finish": 4, "adamw": 5,
-          "apply_update": 6}
+          "apply_update": 6, "ns_single": 7}
 MAX_STEPS = 16
 NOALLOC_SCRATCH_BYTES = 64 << 20
 

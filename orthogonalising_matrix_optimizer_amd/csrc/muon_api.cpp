@@ -62,6 +62,9 @@ struct Plan {
   // muon_step_prepare only and read by captured steps, so no eager call on the
   // same workspace can change what a replay reads)
   size_t off_desc = 0, off_pprefix = 0, off_fprefix = 0, off_fin = 0, tab_bytes = 0;
+  // three words of the single-launch Newton-Schulz path (barrier arrivals,
+  // blocks done, failure flag): zero in every table sent
+  size_t off_sync = 0;
   size_t off_tab[2] = {0, 0};
   size_t total = 0;
   std::vector<int64_t> pprefix, fprefix;
@@ -174,6 +177,8 @@ void build_plan(const int64_t* rows, const int64_t* cols, int n, int xdt, Plan& 
   off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
   p.off_fprefix = off;
   off = align_up(off + sizeof(int64_t) * size_t(n + 1), kAlign);
+  p.off_sync = off;
+  off = align_up(off + 4 * sizeof(uint32_t), kAlign);
   // fused update table: the parameter matrices in group order
   p.off_fin = off;
   off = align_up(off + sizeof(FinDesc) * size_t(n), kAlign);
@@ -439,6 +444,36 @@ bool fold_ok(float num, float den) {
   return std::isfinite(r) && std::fabs(r) <= 0x1p32f && std::fabs(den) >= 0x1p-32f;
 }
 
+// Small problems (64-wide bf16 tiles, at most four tiles per block and
+// product) can run all iterations in one launch, on request
+// (MUON_NS_SINGLE_LAUNCH=1): on MI355X its grid-wide barriers cost more than
+// the kernel boundaries they replace (one 256 x 512 matrix: 0.150 ms per step
+// against 0.082 ms with one launch per product), so it is not the default.
+bool single_launch_ok(const Plan& p, int steps, bool fin) {
+  if (fin || steps <= 0 || steps > kSmallMaxSteps || p.ts != 64 || p.xdt != MUON_BF16 ||
+      p.groups.size() > size_t(kMaxGroups))
+    return false;
+  const char* e = std::getenv("MUON_NS_SINGLE_LAUNCH");
+  if (!e || std::strcmp(e, "1") != 0) return false;
+  for (int ph = 0; ph < 3; ++ph) {
+    int64_t t = 0;
+    for (auto& g : p.groups) {
+      const int64_t tm = g.mp / p.ts, tn = g.np / p.ts;
+      t += int64_t(g.mats.size()) * (ph == 2 ? tm * tn : tm * (tm + 1) / 2);
+    }
+    if (t > 4 * int64_t(kCUs)) return false;
+  }
+  return true;
+}
+
+// Polls of the single launch's barrier before a block gives up; the
+// MUON_NS_SPIN_LIMIT override exists to force the failure path (0: fail at
+// once).
+uint32_t spin_limit() {
+  if (const char* e = std::getenv("MUON_NS_SPIN_LIMIT")) return uint32_t(std::strtoul(e, nullptr, 10));
+  return 1u << 20;
+}
+
 bool folding_safe(const float* coeffs, int steps) {
   if (!coeffs) return true;   // quintic
   for (int j = 0; j < steps; ++j) {
@@ -467,6 +502,42 @@ bool update_fusable(const Plan& p, const muon_mat* params, int n, bool cautious,
 hipError_t run_ns(const Plan& p, char* ws, const char* tab, const float* coeffs, int steps,
                   float eps, hipStream_t s, int* final_buf, bool fin = false, float lr = 0.f,
                   float lrwd = 0.f) {
+  if (single_launch_ok(p, steps, fin)) {
+    SmallArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.ngroups = int(p.groups.size());
+    sa.steps = steps;
+    sa.eps = eps;
+    sa.spin_limit = spin_limit();
+    for (int j = 0; j < steps; ++j)
+      for (int c = 0; c < 3; ++c) sa.coef[j][c] = coeffs[3 * j + c];
+    sa.sync = reinterpret_cast<uint32_t*>(const_cast<char*>(tab) + p.off_sync);
+    int64_t most = 0;
+    for (size_t gi = 0; gi < p.groups.size(); ++gi) {
+      const GroupPlan& g = p.groups[gi];
+      SmallGroup& d = sa.g[gi];
+      d.x0 = ws + g.off_x0; d.x1 = ws + g.off_x1; d.a = ws + g.off_a; d.b = ws + g.off_b;
+      d.partials = reinterpret_cast<const float*>(ws + g.off_part);
+      d.x_elems = g.x_elems; d.a_elems = g.a_elems;
+      d.count = int(g.mats.size()); d.mp = g.mp; d.np = g.np; d.npart = g.npart;
+      d.kg = int(round_up(g.n, 128));
+      d.kp = int(round_up(g.m, 128));
+    }
+    for (int ph = 0; ph < 3; ++ph) {
+      int64_t t = 0;
+      for (auto& g : p.groups) {
+        const int64_t tm = g.mp / p.ts, tn = g.np / p.ts;
+        t += int64_t(g.mats.size()) * (ph == 2 ? tm * tn : tm * (tm + 1) / 2);
+      }
+      most = std::max(most, t);
+    }
+    probe_begin(MUON_PHASE_NS_SINGLE, s);
+    const hipError_t err = launch_ns_small(sa, int(std::min<int64_t>(most, kCUs)), s);
+    probe_end(MUON_PHASE_NS_SINGLE, s);
+    if (err != hipSuccess) return err;
+    *final_buf = steps & 1;
+    return hipSuccess;
+  }
   int cur = 0;
   const bool fold = folding_safe(coeffs, steps);
   for (int j = 0; j < steps; ++j) {
@@ -772,6 +843,7 @@ int step_impl(const muon_mat* params, const muon_mat* grads, muon_state* st, con
     return MUON_E_HIP;
   if (!fused) {
     ea.final_buf = fb;
+    ea.ns_err = reinterpret_cast<const uint32_t*>(tab + p.off_sync) + 2;
     ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_fprefix);
     probe_begin(MUON_PHASE_FINISH, s);
     err = launch_finish(ea, p.fprefix[n], s);
@@ -921,6 +993,7 @@ int muon_orthogonalize(const muon_mat* in, const muon_mat* out, int32_t n, const
   int fb = 0;
   if (run_ns(p, ws, tab, coeffs, steps, o.eps, s, &fb) != hipSuccess) return MUON_E_HIP;
   ea.final_buf = fb;
+  ea.ns_err = reinterpret_cast<const uint32_t*>(tab + p.off_sync) + 2;
   ea.prefix = reinterpret_cast<const int64_t*>(tab + p.off_fprefix);
   probe_begin(MUON_PHASE_FINISH, s);
   err = launch_finish(ea, p.fprefix[n], s);
@@ -992,7 +1065,7 @@ int muon_ema_blend(const muon_mat* out, const muon_mat* params, const muon_state
 }
 
 int muon_probe_arm(int32_t phase, int32_t capacity) {
-  if (phase < 0 || phase > MUON_PHASE_APPLY_UPDATE || capacity < 1 || capacity > 65536)
+  if (phase < 0 || phase > MUON_PHASE_NS_SINGLE || capacity < 1 || capacity > 65536)
     return MUON_E_HPARAM;
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto e : g_probe.ev0) (void)hipEventDestroy(e);
@@ -1055,9 +1128,13 @@ int muon_plan_info(const muon_mat* params, int32_t n, const muon_options* opt, i
     const bool fused = update_fusable(p, params, n, opt && opt->cautious,
                                       opt && opt->beta_ema >= 0.f, false, coeffs, steps);
     int l = n > 0 ? (fused ? 1 : 2) : 0;
-    for (int j = 0; j < steps && n > 0; ++j) {
-      const bool poly = !coeffs || coeffs[3 * j + 2] != 0.f;
-      l += sets * (poly ? 3 : 2);
+    if (n > 0 && single_launch_ok(p, steps, fused)) {
+      l += 1;
+    } else {
+      for (int j = 0; j < steps && n > 0; ++j) {
+        const bool poly = !coeffs || coeffs[3 * j + 2] != 0.f;
+        l += sets * (poly ? 3 : 2);
+      }
     }
     *launches_per_step = l;
   }

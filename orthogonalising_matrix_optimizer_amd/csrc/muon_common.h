@@ -67,6 +67,8 @@ struct ElemArgs {
   int32_t ema_on, ema_first;
   int32_t final_buf;       // iterate buffer holding O (0 -> x0, 1 -> x1)
   int32_t scale_o;         // steps == 0: O = s * X0
+  const uint32_t* ns_err;  // finish: nonzero flag here = the iterations failed
+                           // (single-launch path), O is taken as NaN; or null
 };
 
 // A parameter matrix updated in the last APPLY's epilogue (plain update,
@@ -122,6 +124,30 @@ struct GemmArgs {
                           // coefficient ratios that could overflow them)
 };
 
+// All Newton-Schulz iterations of a small problem (64-wide bf16 tiles) in one
+// launch: per effective-shape group the workspace buffers, per iteration the
+// coefficients; the blocks take the tiles of each product in turn and meet at
+// a grid-wide barrier between products.
+constexpr int kSmallMaxSteps = 16;
+struct SmallGroup {
+  const void* x0;         // iterate buffers (ping-pong), bf16 mp x np
+  const void* x1;
+  void* a;                // Gram matrix A, bf16 mp x mp
+  void* b;                // polynomial B, bf16 mp x mp
+  const float* partials;  // norm partials of the first iteration
+  int64_t x_elems, a_elems;
+  int32_t count, mp, np, npart;
+  int32_t kg, kp;         // K loop lengths: GRAM (n rounded to 128), POLY and APPLY (m)
+};
+struct SmallArgs {
+  SmallGroup g[kMaxGroups];
+  int32_t ngroups, steps;
+  float eps;
+  uint32_t spin_limit;        // barrier polls before a block gives up (sets the flag)
+  float coef[kSmallMaxSteps][3];
+  uint32_t* sync;             // [0] barrier arrivals, [1] blocks done, [2] failure flag
+};
+
 }  // namespace muon
 
 // Launchers (defined in the .hip sources; called by the C ABI layer).
@@ -161,6 +187,7 @@ hipError_t launch_blend(const ElemArgs& a, int64_t blocks, float wf, float owf,
 hipError_t launch_put_table(void* dst, const uint8_t* bytes, size_t n, hipStream_t s);
 // phase: 0 GRAM, 1 POLY, 2 APPLY; ts: tile edge (64, 128; 256 for bf16 only);
 // waves: 8 for 256-wide tiles, else 4.
+hipError_t launch_ns_small(const SmallArgs& a, int blocks, hipStream_t s);
 hipError_t launch_gemm(int phase, int xdt, int ts, int waves, const GemmArgs& a,
                        int64_t blocks, hipStream_t s);
 }  // namespace muon

@@ -309,6 +309,13 @@ __device__ __forceinline__ void prepare_strip(const ElemArgs& a, const MatDesc& 
   if (t == 0) glb(d.partials)[local] = tot;
 }
 
+// Whether the single-launch Newton-Schulz path marked this step failed (its
+// grid barrier gave up): O is then taken as NaN, so the failure shows.
+__device__ __forceinline__ bool ns_failed(const ElemArgs& a) {
+  return a.ns_err != nullptr &&
+         __hip_atomic_load(a.ns_err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
 template <bool STEP, bool CAUT, bool EMA, int NT>
 __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d, int local,
                                              float* red) {
@@ -352,6 +359,12 @@ __device__ __forceinline__ void finish_strip(const ElemArgs& a, const MatDesc& d
     for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[ps][k] = s * o[ps][k];
+  }
+  if (ns_failed(a)) {
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[ps][k] = __builtin_nanf("");
   }
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
@@ -565,6 +578,12 @@ __global__ __launch_bounds__(NT) void k_finish(ElemArgs a) {
     for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[ps][k] = s * o[ps][k];
+  }
+  if (ns_failed(a)) {
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[ps][k] = __builtin_nanf("");
   }
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {

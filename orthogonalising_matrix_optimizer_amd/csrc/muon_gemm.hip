@@ -162,7 +162,10 @@ __device__ __forceinline__ u32x4_t make_desc(const void* base, uint32_t bytes) {
 
 // LDS byte address of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+  // the low half of a flat address in the LDS aperture is the LDS address (an
+  // address-space cast here adds a null check that one compiler release
+  // fails to select in the single-launch kernel)
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 // One 1 KiB LDS-DMA load: lane L copies 16 bytes from global offset
@@ -959,6 +962,133 @@ __global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_gemm(GemmArgs args) {
   gemm_tile<XDT, MODE, TS, WGP, WGQ, FIN>(G, mat, tP, tQ, cf, smem, red);
 }
 
+// ---- all Newton-Schulz iterations of a small problem in one launch
+//
+// Grid-wide barrier between products.  Every thread releases its global
+// stores at device scope (written back past its XCD's L2), one thread per
+// block counts in and polls the arrival counter, and every thread then
+// acquires at device scope (stale lines in its CU's and XCD's caches are
+// dropped) before it reads what other blocks wrote.  The poll is bounded: a
+// block that gives up sets the failure flag (the finish kernel then writes
+// NaN) and goes on, so every block reaches the end of the kernel.  A limit of
+// zero fails at once (the host forces the failure path that way).
+__device__ __forceinline__ void grid_barrier(uint32_t* sync, uint32_t target, uint32_t limit) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t n = 0;
+    while (limit == 0u ||
+           __hip_atomic_load(&sync[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (n++ >= limit) {
+        __hip_atomic_store(&sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  __threadfence();
+}
+
+// The blocks take the tiles of each product (GRAM, POLY unless c = 0, APPLY)
+// of each iteration in turn, block-strided over all groups, with the tile
+// code of the multi-launch path (64-wide bf16 tiles), so the results are bit
+// for bit those of the separate launches.  The last block out resets the
+// counters for the next launch on the stream.
+template <int WGP, int WGQ>
+__global__ __launch_bounds__(64 * WGP * WGQ, 1) void k_ns_small(SmallArgs args) {
+  constexpr int TS = 64, CPR = Ty<kBF16>::CPR, NST = stages<kBF16, TS>(), NW = WGP * WGQ;
+  constexpr int OPB = TS * CPR * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * 2 * OPB];
+  __shared__ float red[NW];
+  const int nb = static_cast<int>(gridDim.x);
+  uint32_t target = 0;
+  int cur = 0;
+  for (int j = 0; j < args.steps; ++j) {
+    TileCoef cf;
+    cf.ca = args.coef[j][0]; cf.cb = args.coef[j][1]; cf.cc = args.coef[j][2];
+    const bool poly = cf.cc != 0.f;
+    cf.cbb = poly ? 1.f : cf.cb;
+    cf.eps = args.eps; cf.first = j == 0;
+    cf.lr = 0.f; cf.lrwd = 0.f; cf.ablk = 0; cf.nofold = 0;
+    for (int ph = GRAM; ph <= APPLY; ++ph) {
+      if (ph == POLY && !poly) continue;
+#pragma unroll 1
+      for (int t = static_cast<int>(blockIdx.x);; t += nb) {
+        // group, matrix and tile of work item t (constant-index selection
+        // keeps the group table in kernel-argument space)
+        SmallGroup sg = args.g[0];
+        int rem = t, tiles = 0, found = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxGroups; ++k) {
+          if (k < args.ngroups && !found) {
+            const int tm = args.g[k].mp / TS, tn = args.g[k].np / TS;
+            const int tk = ph == APPLY ? tm * tn : tm * (tm + 1) / 2;
+            if (rem < args.g[k].count * tk) {
+              sg = args.g[k];
+              tiles = tk;
+              found = 1;
+            } else {
+              rem -= args.g[k].count * tk;
+            }
+          }
+        }
+        if (!found) break;
+        const int mat = rem / tiles, tile = rem - mat * tiles;
+        const int tm = sg.mp / TS, tn = sg.np / TS;
+        GemmGroup G;
+        G.count = sg.count; G.mp = sg.mp; G.np = sg.np; G.tiles = tiles; G.block_base = 0;
+        G.partials = sg.partials; G.p_stride = sg.npart; G.npartials = sg.npart;
+        G.fin = nullptr; G.bop = nullptr; G.b_stride = 0;
+        const void* xc = cur ? sg.x1 : sg.x0;
+        void* xn = const_cast<void*>(cur ? sg.x0 : sg.x1);
+        int tP, tQ;
+        if (ph == APPLY) {
+          G.xin = xc; G.bop = poly ? sg.b : sg.a; G.out = xn;
+          G.in_stride = sg.x_elems; G.b_stride = sg.a_elems; G.out_stride = sg.x_elems;
+          G.kdim = sg.kp;
+          tP = tile % tn;
+          tQ = tile / tn;
+        } else {
+          if (ph == GRAM) {
+            G.xin = xc; G.out = sg.a; G.in_stride = sg.x_elems; G.out_stride = sg.a_elems;
+            G.kdim = sg.kg;
+          } else {
+            G.xin = sg.a; G.out = sg.b; G.in_stride = sg.a_elems; G.out_stride = sg.a_elems;
+            G.kdim = sg.kp;
+          }
+          int bi = 0, r = tile;
+          while (r >= tm - bi) { r -= tm - bi; ++bi; }
+          tP = bi;
+          tQ = bi + r;
+        }
+        if (ph == GRAM) gemm_tile<kBF16, GRAM, TS, WGP, WGQ, false>(G, mat, tP, tQ, cf, smem, red);
+        else if (ph == POLY) gemm_tile<kBF16, POLY, TS, WGP, WGQ, false>(G, mat, tP, tQ, cf, smem, red);
+        else gemm_tile<kBF16, APPLY, TS, WGP, WGQ, false>(G, mat, tP, tQ, cf, smem, red);
+        // the next tile's first loads refill stage buffers that a slower wave
+        // may still be reading
+        __syncthreads();
+      }
+      if (!(j == args.steps - 1 && ph == APPLY)) {
+        target += static_cast<uint32_t>(nb);
+        grid_barrier(args.sync, target, args.spin_limit);
+      }
+    }
+    cur ^= 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(&args.sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == static_cast<uint32_t>(nb) - 1u) {
+      // every other block is past its last poll
+      __hip_atomic_store(&args.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&args.sync[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 template <int XDT, int MODE>
 hipError_t launch_ts(int ts, int waves, const GemmArgs& a, int64_t blocks, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(blocks));
@@ -993,6 +1123,14 @@ hipError_t launch_ts(int ts, int waves, const GemmArgs& a, int64_t blocks, hipSt
 }
 
 }  // namespace
+
+hipError_t launch_ns_small(const SmallArgs& a, int blocks, hipStream_t s) {
+  if (blocks <= 0 || a.steps <= 0) return hipSuccess;
+  if (a.steps > kSmallMaxSteps || a.ngroups < 1 || a.ngroups > kMaxGroups || !a.sync)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_ns_small<2, 2>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(int phase, int xdt, int ts, int waves, const GemmArgs& a,
                        int64_t blocks, hipStream_t s) {

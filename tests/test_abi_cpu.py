@@ -262,7 +262,7 @@ def test_orthogonalize_and_blend_validation(lib):
     assert lib.muon_ema_blend(p, p, st, 0.35, None) == E["MUON_E_STATE"]
     assert lib.muon_ema_blend(p, p, st, 1.5, None) == E["MUON_E_HPARAM"]
     assert lib.muon_probe_arm(9, 4) == E["MUON_E_HPARAM"]
-    assert lib.muon_probe_arm(7, 4) == E["MUON_E_HPARAM"]
+    assert lib.muon_probe_arm(8, 4) == E["MUON_E_HPARAM"]
     # phase 6 (the APPLY launch that carries the update) is a phase; arming it
     # creates HIP events, which fails without a GPU
     assert lib.muon_probe_arm(6, 4) != E["MUON_E_HPARAM"]
@@ -306,9 +306,30 @@ def test_plan_groups_and_launches(lib):
     assert ws % 256 == 0
     ng, ts, lps, ws32 = _plan(lib, [(256, 512)], ns=_lib.MUON_F32)
     assert ng == 1 and ts == 64            # one small matrix: smallest tiles
+    assert lps == 2 + 5 * 3                # fp32 operands: one launch per product
     assert ws32 >= 4 * (2 * 256 * 512 + 2 * 256 * 256)
     assert _plan(lib, gen.moe_share_shapes())[0] == 2
     assert _plan(lib, [(5, 3), (3, 5), (7, 7)])[0] == 2
+
+
+def test_small_problems_can_run_the_iterations_in_one_launch(lib, monkeypatch):
+    # default: one launch per product
+    ng, ts, lps, _ = _plan(lib, [(256, 512)])
+    assert ts == 64 and lps == 2 + 5 * 3
+    assert _plan(lib, [(256, 512)], coeffs=[gen.CUBIC] * 5)[2] == 2 + 5 * 2
+    # on request (read at every call), 64-wide tiles with bf16 operands:
+    # prepare, one launch for all products, finish (the plain update needs
+    # 256-wide tiles to run in an epilogue)
+    monkeypatch.setenv("MUON_NS_SINGLE_LAUNCH", "1")
+    assert _plan(lib, [(256, 512)])[2] == 3
+    assert _plan(lib, [(256, 512)], coeffs=[gen.CUBIC] * 5)[2] == 3
+    assert _plan(lib, [(256, 512)], steps=16)[2] == 3
+    assert _plan(lib, [(256, 512)], ns=_lib.MUON_F32)[2] == 2 + 5 * 3
+    # more than 1024 tiles in a product: separate launches
+    monkeypatch.setenv("MUON_TILE", "64")
+    many = [(512, 512)] * 40                # 40 x 36 = 1440 GRAM tiles of 64
+    assert _plan(lib, many)[1] == 64
+    assert _plan(lib, many)[2] == 2 + 5 * 3
 
 
 def test_workspace_bytes_rejects_bad_shapes(lib):

@@ -12,6 +12,8 @@ from workloads import gen
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(768, 3072), (3072, 768), (768, 768), (200, 333), (333, 200), (64, 1000)]
+# small enough for 64-wide tiles: all iterations in one launch on request
+SMALL = [(256, 512), (512, 256), (200, 333), (64, 64)]
 
 
 @pytest.fixture(autouse=True)
@@ -21,16 +23,16 @@ def _need_gpu():
     mo._lib.load()
 
 
-def _params(seed):
+def _params(seed, shapes=SHAPES):
     dev = torch.device("cuda")
     return [gen.torch_param_matrix(r, c, seed, i, dev, dtype=torch.bfloat16)
-            for i, (r, c) in enumerate(SHAPES)]
+            for i, (r, c) in enumerate(shapes)]
 
 
-def _grads(seed, step):
+def _grads(seed, step, shapes=SHAPES):
     dev = torch.device("cuda")
     return [gen.torch_grad_matrix(r, c, seed, step, i, dev, rms=1e-3, dtype=torch.bfloat16)
-            for i, (r, c) in enumerate(SHAPES)]
+            for i, (r, c) in enumerate(shapes)]
 
 
 def _eager_work():
@@ -44,21 +46,21 @@ def _same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-def _run(kw, eager_first, replays):
-    pa = _params(7)
+def _run(kw, eager_first, replays, shapes=SHAPES):
+    pa = _params(7, shapes)
     pb = [p.clone() for p in pa]
     A = mo.Muon(pa, **kw)
     B = mo.Muon(pb, **kw)
-    static = [torch.empty_like(g) for g in _grads(7, 0)]
+    static = [torch.empty_like(g) for g in _grads(7, 0, shapes)]
     t = 0
     for _ in range(eager_first):
-        g = _grads(7, t)
+        g = _grads(7, t, shapes)
         A.step(g)
         B.step(g)
         t += 1
     graph = B.graph(static)
     for _ in range(replays):
-        g = _grads(7, t)
+        g = _grads(7, t, shapes)
         for dst, src in zip(static, g):
             dst.copy_(src)
         A.step(g)
@@ -85,6 +87,15 @@ def test_graph_replays_match_eager_anvil_ema():
     kw = dict(lr=0.02, wd=0.1, beta=0.9, steps=6, beta_slow=0.99, cautious=True,
               beta_ema=0.99, ema_start=1)
     _run(kw, eager_first=2, replays=5)
+
+
+def test_graph_replays_match_eager_single_launch(monkeypatch):
+    """A small set whose iterations run in one launch with grid barriers: the
+    barrier counters reset themselves at the end of every replay."""
+    announce("graph: small set, all iterations in one launch, eight replays")
+    monkeypatch.setenv("MUON_NS_SINGLE_LAUNCH", "1")
+    assert mo.plan_info(SMALL, 5)["launches_per_step"] == 3
+    _run(dict(lr=0.02, wd=0.01, beta=0.95, steps=5), eager_first=1, replays=8, shapes=SMALL)
 
 
 def test_graph_refused_before_average_starts():

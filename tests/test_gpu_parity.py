@@ -100,6 +100,90 @@ def test_mixed_coefficient_table(tile, ns, tol):
         assert sigma_dev(host(o), ref) <= TOL_SIGMA, u.shape
 
 
+# small matrices in at most eight effective-shape groups: 64-wide tiles, all
+# iterations in one launch when MUON_NS_SINGLE_LAUNCH=1
+SINGLE = [(256, 512), (512, 256), (200, 333), (129, 65), (17, 257), (300, 300), (64, 1000),
+          (8, 8)]
+
+
+@pytest.mark.parametrize("kind", ["quintic", "cubic", "mixed"])
+def test_single_launch_matches_separate_launches(kind, monkeypatch):
+    """The one-launch path computes every tile with the code of the separate
+    launches, so O must be the same bit for bit; a product that read another
+    block's output before the barrier made it visible would differ.  Twenty
+    calls in a row on one workspace (the counters reset themselves) all
+    match, and O matches the oracle."""
+    announce(f"single launch vs one launch per product, {kind}")
+    table = (np.array([gen.QUINTIC, gen.CUBIC, (1.25, 0.0, 0.0), gen.QUINTIC, gen.CUBIC])
+             if kind == "mixed" else _table(kind, 5))
+    assert mo.plan_info(SINGLE, len(table), table)["launches_per_step"] > 3
+    us = [gen.grad_matrix(r, c, 3, 0, i).astype(np.float32) for i, (r, c) in enumerate(SINGLE)]
+    ins = [dev_f32(u) for u in us]
+
+    def run():
+        outs = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in ins]
+        mo.orthogonalize(ins, outs, coeffs=table, steps=len(table), ns_dtype="bf16")
+        torch.cuda.synchronize()
+        return outs
+
+    want = run()
+    monkeypatch.setenv("MUON_NS_SINGLE_LAUNCH", "1")
+    assert mo.plan_info(SINGLE, len(table), table)["launches_per_step"] == 3
+    for rep in range(20):
+        got = run()
+        for o, w, sh in zip(got, want, SINGLE):
+            assert torch.equal(o, w), (rep, sh)
+    for u, o in zip(us, want):
+        ref = orc.orthogonalize(u.astype(np.float64), table)
+        assert orc.rel_fro(host(o), ref) <= TOL_BF16, u.shape
+        assert sigma_dev(host(o), ref) <= TOL_SIGMA, u.shape
+
+
+def test_single_launch_step_twins(monkeypatch):
+    """Optimizer steps through the one-launch path and through separate
+    launches on identical buffers stay bitwise equal over five steps."""
+    announce("single launch: optimizer twins over five steps")
+    shapes = SINGLE[:4]
+    gs, ws = _make(shapes, "bf16")
+    pa = [_dev(w) for w in ws]
+    pb = [p.clone() for p in pa]
+    a = mo.Muon(pa, lr=0.02, wd=0.1, beta=0.95, steps=5)
+    b = mo.Muon(pb, lr=0.02, wd=0.1, beta=0.95, steps=5)
+    for t in range(5):
+        grads = [_dev(gen.bf16_bits_from_f32(gen.grad_matrix(r, c, 1, t, i, 1e-3).astype(np.float32)))
+                 for i, (r, c) in enumerate(shapes)]
+        monkeypatch.setenv("MUON_NS_SINGLE_LAUNCH", "1")
+        a.step(grads)
+        monkeypatch.delenv("MUON_NS_SINGLE_LAUNCH")
+        b.step(grads)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert torch.equal(pa[i], pb[i]), (t, shapes[i])
+
+
+def test_single_launch_failure_is_never_silent(monkeypatch):
+    """A block that gives up waiting at a grid barrier (forced from the host
+    with a zero poll limit, so no wait hangs) marks the step failed and every
+    O comes out NaN; the next call, with the normal limit, is correct again."""
+    announce("single launch: forced barrier failure")
+    shapes = SINGLE[:3]
+    us = [gen.grad_matrix(r, c, 4, 0, i).astype(np.float32) for i, (r, c) in enumerate(shapes)]
+    ins = [dev_f32(u) for u in us]
+    outs = [torch.zeros(t.shape, dtype=torch.float32, device="cuda") for t in ins]
+    monkeypatch.setenv("MUON_NS_SINGLE_LAUNCH", "1")
+    monkeypatch.setenv("MUON_NS_SPIN_LIMIT", "0")
+    mo.orthogonalize(ins, outs, coeffs=_table("quintic", 5), steps=5, ns_dtype="bf16")
+    torch.cuda.synchronize()
+    for o in outs:
+        assert bool(torch.isnan(o).all())
+    monkeypatch.delenv("MUON_NS_SPIN_LIMIT")
+    mo.orthogonalize(ins, outs, coeffs=_table("quintic", 5), steps=5, ns_dtype="bf16")
+    torch.cuda.synchronize()
+    for u, o in zip(us, outs):
+        ref = orc.orthogonalize(u.astype(np.float64), _table("quintic", 5))
+        assert orc.rel_fro(host(o), ref) <= TOL_BF16, u.shape
+
+
 @pytest.mark.parametrize("tile", [256], indirect=True)
 def test_tiny_coefficient_ratios_run_unfolded(tile):
     """The 256-wide bf16 products fold the term bA (or aX) into their
