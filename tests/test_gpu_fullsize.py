@@ -14,7 +14,7 @@ import torch
 
 import orthogonalising_matrix_optimizer_amd as mo
 from oracle import muon_oracle as orc
-from tests.gpu_helpers import TOL_BF16, TOL_SIGMA, announce, host, sigma_dev
+from tests.gpu_helpers import TOL_BF16, TOL_F32, TOL_SIGMA, announce, host, sigma_dev
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -35,10 +35,10 @@ def _bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _check_o(O, M, coeffs, shape):
+def _check_o(O, M, coeffs, shape, tol=TOL_BF16):
     ref = orc.orthogonalize(M.astype(np.float64), coeffs)
     err = orc.rel_fro(O, ref)
-    assert err <= TOL_BF16, (shape, err)
+    assert err <= tol, (shape, err)
     assert sigma_dev(O, ref) <= TOL_SIGMA, shape
 
 
@@ -66,6 +66,27 @@ def test_gpt124m_one_step_full_size():
         np.testing.assert_array_equal(host(params[i]), want)
         _check_o(O, M, coeffs, shapes[i])
     assert opt.step_count == 1
+
+
+def test_gpt124m_fp32_iterations_full_size():
+    """The fp32 Newton-Schulz path (fp32 MFMA, 128-wide tiles) on the whole
+    124M set: O of every matrix within the fp32 tolerance of the oracle."""
+    announce("full size: gpt124m one step, fp32 iterations")
+    ms = gen.SETS["gpt124m"]
+    shapes = list(ms.shapes)
+    coeffs = gen.coeff_table(ms.coeffs, ms.steps)
+    inputs = gen.make_inputs(ms, seed=2)
+    params = [_dev_bits(w) for _, w in inputs]
+    grads = [_dev_bits(g) for g, _ in inputs]
+    opt = mo.Muon(params, lr=ms.lr, wd=ms.wd, beta=ms.beta, steps=ms.steps, coeffs=coeffs,
+                  ns_dtype="f32", diagnostics=True)
+    assert mo.plan_info(shapes, ms.steps, coeffs, ns_dtype="f32")["tile"] == 128
+    opt.step(grads)
+    torch.cuda.synchronize()
+    for i, (g, _) in enumerate(inputs):
+        M = orc.momentum_f32(np.zeros(shapes[i], np.float32), gen.f32_from_bf16_bits(g), ms.beta)
+        np.testing.assert_array_equal(host(opt.mom[i]), M)
+        _check_o(host(opt.update[i]), M, coeffs, shapes[i], tol=TOL_F32)
 
 
 def test_gpt124m_anvil_ten_steps_full_size():

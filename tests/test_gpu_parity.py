@@ -104,20 +104,26 @@ def test_mixed_coefficient_table(tile, ns, tol):
 # iterations in one launch when MUON_NS_SINGLE_LAUNCH=1
 SINGLE = [(256, 512), (512, 256), (200, 333), (129, 65), (17, 257), (300, 300), (64, 1000),
           (8, 8)]
+# 64-wide tiles forced: up to 960 tiles per product, so most blocks take
+# several tiles of a product in turn
+MANY = [(512, 512)] * 12 + [(256, 768)] * 4
 
 
-@pytest.mark.parametrize("kind", ["quintic", "cubic", "mixed"])
-def test_single_launch_matches_separate_launches(kind, monkeypatch):
+@pytest.mark.parametrize("kind,shapes,force", [("quintic", SINGLE, None), ("cubic", SINGLE, None),
+                                               ("mixed", SINGLE, None), ("quintic", MANY, "64")])
+def test_single_launch_matches_separate_launches(kind, shapes, force, monkeypatch):
     """The one-launch path computes every tile with the code of the separate
     launches, so O must be the same bit for bit; a product that read another
     block's output before the barrier made it visible would differ.  Twenty
     calls in a row on one workspace (the counters reset themselves) all
     match, and O matches the oracle."""
-    announce(f"single launch vs one launch per product, {kind}")
+    announce(f"single launch vs one launch per product, {kind}, {len(shapes)} matrices")
+    if force:
+        monkeypatch.setenv("MUON_TILE", force)
     table = (np.array([gen.QUINTIC, gen.CUBIC, (1.25, 0.0, 0.0), gen.QUINTIC, gen.CUBIC])
              if kind == "mixed" else _table(kind, 5))
-    assert mo.plan_info(SINGLE, len(table), table)["launches_per_step"] > 3
-    us = [gen.grad_matrix(r, c, 3, 0, i).astype(np.float32) for i, (r, c) in enumerate(SINGLE)]
+    assert mo.plan_info(shapes, len(table), table)["launches_per_step"] > 3
+    us = [gen.grad_matrix(r, c, 3, 0, i).astype(np.float32) for i, (r, c) in enumerate(shapes)]
     ins = [dev_f32(u) for u in us]
 
     def run():
@@ -128,10 +134,11 @@ def test_single_launch_matches_separate_launches(kind, monkeypatch):
 
     want = run()
     monkeypatch.setenv("MUON_NS_SINGLE_LAUNCH", "1")
-    assert mo.plan_info(SINGLE, len(table), table)["launches_per_step"] == 3
-    for rep in range(20):
+    info = mo.plan_info(shapes, len(table), table)
+    assert info["launches_per_step"] == 3 and info["tile"] == 64
+    for rep in range(20 if force is None else 5):
         got = run()
-        for o, w, sh in zip(got, want, SINGLE):
+        for o, w, sh in zip(got, want, shapes):
             assert torch.equal(o, w), (rep, sh)
     for u, o in zip(us, want):
         ref = orc.orthogonalize(u.astype(np.float64), table)
