@@ -362,6 +362,8 @@ def main():
                          "(single matrix, AdamW, graph replay)")
     ap.add_argument("--single-only", action="store_true",
                     help="only time the single 256x512 matrix step (eager and replayed)")
+    ap.add_argument("--adamw-only", action="store_true",
+                    help="only time the AdamW step over the 124M model's non-matrix parameters")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -385,6 +387,9 @@ def main():
         print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
         return
 
+    if args.adamw_only:
+        print(json.dumps(adamw_times(gen, mo, dev, max(args.steps, 20))), flush=True)
+        return
     if args.single_only:
         print(json.dumps(single_matrix_times(gen, mo, dev, args.steps,
                                              with_oracle=not args.no_cpu_baseline)), flush=True)
