@@ -444,6 +444,20 @@ bool fold_ok(float num, float den) {
   return std::isfinite(r) && std::fabs(r) <= 0x1p32f && std::fabs(den) >= 0x1p-32f;
 }
 
+// Most tiles of any one product (GRAM, POLY, APPLY) of a plan.
+int64_t max_phase_tiles(const Plan& p) {
+  int64_t most = 0;
+  for (int ph = 0; ph < 3; ++ph) {
+    int64_t t = 0;
+    for (auto& g : p.groups) {
+      const int64_t tm = g.mp / p.ts, tn = g.np / p.ts;
+      t += int64_t(g.mats.size()) * (ph == 2 ? tm * tn : tm * (tm + 1) / 2);
+    }
+    most = std::max(most, t);
+  }
+  return most;
+}
+
 // Small problems (64-wide bf16 tiles, at most four tiles per block and
 // product) can run all iterations in one launch, on request
 // (MUON_NS_SINGLE_LAUNCH=1): on MI355X its grid-wide barriers cost more than
@@ -455,15 +469,7 @@ bool single_launch_ok(const Plan& p, int steps, bool fin) {
     return false;
   const char* e = std::getenv("MUON_NS_SINGLE_LAUNCH");
   if (!e || std::strcmp(e, "1") != 0) return false;
-  for (int ph = 0; ph < 3; ++ph) {
-    int64_t t = 0;
-    for (auto& g : p.groups) {
-      const int64_t tm = g.mp / p.ts, tn = g.np / p.ts;
-      t += int64_t(g.mats.size()) * (ph == 2 ? tm * tn : tm * (tm + 1) / 2);
-    }
-    if (t > 4 * int64_t(kCUs)) return false;
-  }
-  return true;
+  return max_phase_tiles(p) <= 4 * int64_t(kCUs);
 }
 
 // Polls of the single launch's barrier before a block gives up; the
@@ -512,7 +518,6 @@ hipError_t run_ns(const Plan& p, char* ws, const char* tab, const float* coeffs,
     for (int j = 0; j < steps; ++j)
       for (int c = 0; c < 3; ++c) sa.coef[j][c] = coeffs[3 * j + c];
     sa.sync = reinterpret_cast<uint32_t*>(const_cast<char*>(tab) + p.off_sync);
-    int64_t most = 0;
     for (size_t gi = 0; gi < p.groups.size(); ++gi) {
       const GroupPlan& g = p.groups[gi];
       SmallGroup& d = sa.g[gi];
@@ -523,16 +528,9 @@ hipError_t run_ns(const Plan& p, char* ws, const char* tab, const float* coeffs,
       d.kg = int(round_up(g.n, 128));
       d.kp = int(round_up(g.m, 128));
     }
-    for (int ph = 0; ph < 3; ++ph) {
-      int64_t t = 0;
-      for (auto& g : p.groups) {
-        const int64_t tm = g.mp / p.ts, tn = g.np / p.ts;
-        t += int64_t(g.mats.size()) * (ph == 2 ? tm * tn : tm * (tm + 1) / 2);
-      }
-      most = std::max(most, t);
-    }
+    // at most one block per CU: every block must be resident for the barriers
     probe_begin(MUON_PHASE_NS_SINGLE, s);
-    const hipError_t err = launch_ns_small(sa, int(std::min<int64_t>(most, kCUs)), s);
+    const hipError_t err = launch_ns_small(sa, int(std::min<int64_t>(max_phase_tiles(p), kCUs)), s);
     probe_end(MUON_PHASE_NS_SINGLE, s);
     if (err != hipSuccess) return err;
     *final_buf = steps & 1;
