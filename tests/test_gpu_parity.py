@@ -350,6 +350,37 @@ def test_step_matches_oracle(dtype, ns):
     assert opt.step_count == 1
 
 
+@pytest.mark.parametrize("pdt,gdt", [("bf16", "f32"), ("f32", "bf16")])
+def test_step_with_mixed_parameter_and_gradient_types(pdt, gdt):
+    """bf16 weights with fp32 gradients (accumulated in fp32) and the
+    reverse: the momentum takes the gradient's values exactly, O is within the
+    bf16-path tolerance of the oracle and W is exactly the oracle's fp32
+    update of the GPU's own O, stored in the weight's type."""
+    announce(f"step params {pdt}, grads {gdt}")
+    shapes = [(256, 512), (512, 256), (200, 333)]
+    gf = [gen.grad_matrix(r, c, 6, 0, i, 1e-3).astype(np.float32) for i, (r, c) in enumerate(shapes)]
+    wf = [gen.param_matrix(r, c, 6, i).astype(np.float32) for i, (r, c) in enumerate(shapes)]
+    gs = [gen.bf16_bits_from_f32(g) if gdt == "bf16" else g for g in gf]
+    ws = [gen.bf16_bits_from_f32(w) if pdt == "bf16" else w for w in wf]
+    params = [_dev(w) for w in ws]
+    grads = [_dev(g) for g in gs]
+    lr, wd, beta = 0.02, 0.1, 0.95
+    opt = mo.Muon(params, lr=lr, wd=wd, beta=beta, steps=5, coeffs="quintic", diagnostics=True)
+    opt.step(grads)
+    torch.cuda.synchronize()
+    lr32, wd32 = float(np.float32(lr)), float(np.float32(wd))
+    for i in range(len(shapes)):
+        G = _val(gs[i])
+        M = orc.momentum_f32(np.zeros(shapes[i], np.float32), G, beta)
+        np.testing.assert_array_equal(host(opt.mom[i]), M)
+        O = host(opt.update[i])
+        ref = orc.orthogonalize(M.astype(np.float64), _table("quintic", 5))
+        assert orc.rel_fro(O, ref) <= TOL_BF16, shapes[i]
+        assert sigma_dev(O, ref) <= TOL_SIGMA, shapes[i]
+        want = orc.store(orc.update_f32(_val(ws[i]), O, lr32, wd32), pdt)
+        np.testing.assert_array_equal(host(params[i]).astype(np.float64), want)
+
+
 def test_anvil_ten_steps_state_forced():
     """Fast/slow momentum, six map steps, cautious decay, EMA: at every step the
     oracle starts from the GPU's stored state and must agree exactly on the
